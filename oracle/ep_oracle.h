@@ -1,0 +1,93 @@
+/*
+ * ep_oracle.h -- slow, single-threaded CPU oracle for MoE token dispatch and
+ * combine.  TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it; the product path never does.  It shares
+ * no code, header, table or constant generator with the HIP library.
+ *
+ * Pages cited (by title and section):
+ *   [DeepEP overview]  "DeepSeek merilis library open source DeepEP untuk
+ *                      pelatihan dan inferensi MoE" (GeekNews, Indonesian)
+ *   [Perplexity blog]  "Lower latency and higher throughput with multi-node
+ *                      DeepSeek deployment" (Perplexity, Icelandic rendering)
+ *   [torchtitan PR]    "Integrate DeepEP to experimental torchtitan"
+ *
+ * Notation: T tokens, H hidden, k top-k, E experts, R simulated ranks,
+ * El = E/R experts per rank, P = T*k (token, slot) pairs, p = t*k + j.
+ * Rank r owns experts [r*El, (r+1)*El) ([Perplexity blog], "Sérfræðinga-
+ * samsíðun": each GPU holds 256/EP routed experts).
+ *
+ * Data types: indices int32, weights and scales fp32, bf16 as uint16 bit
+ * patterns, FP8 OCP E4M3 ("fn": bias 7, no infinity, max 448) as uint8.
+ *
+ * Every function is a direct transcription of the definition it cites; there
+ * is no blocking, fusion or reordering.
+ */
+#ifndef EP_ORACLE_H
+#define EP_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return 0 when the shapes and every index are acceptable, else a nonzero
+ * code: 1 bad shape (T,k,R<1, E%R, H%8, H%128 under FP8), 2 index outside
+ * [0,E). */
+int oracle_validate(int T, int H, int k, int E, int R, int fp8, const int32_t *idx);
+
+/* Routing layout ([Perplexity blog], "MoE-beirari": dense dispatch/combine
+ * need routing information summed per expert; [DeepEP overview], "Pola
+ * penggunaan...": the handle's per-expert token counts feed the GEMM).
+ * Outputs: cnt[E], off[E+1], rcnt[R], roff[R+1], slot[P], src[P], row[P].
+ * Returns oracle_validate's code for (T,8,k,E,R,0,idx); outputs untouched on
+ * error. */
+int oracle_layout(int T, int k, int E, int R, const int32_t *idx,
+                  int32_t *cnt, int32_t *off, int32_t *rcnt, int32_t *roff,
+                  int32_t *slot, int32_t *src, int32_t *row);
+
+/* BF16 dispatch: recv[r][row[p]][:] = x[t][:] bitwise. recv[r] has H-element
+ * rows. */
+void oracle_dispatch_bf16(int T, int H, int k, int E, int R, const int32_t *idx,
+                          const int32_t *slot, const int32_t *roff,
+                          const uint16_t *x, uint16_t *const *recv);
+
+/* FP8 dispatch with per-128-channel scales ([Perplexity blog], "Magntölun":
+ * activation scales over 128-element vectors, computed on the fly, a scale
+ * tensor of M x ceil_div(K,128)).  recv_q[r] rows of H bytes, recv_s[r] rows
+ * of H/128 floats. */
+void oracle_dispatch_fp8(int T, int H, int k, int E, int R, const int32_t *idx,
+                         const int32_t *slot, const int32_t *roff,
+                         const uint16_t *x, uint8_t *const *recv_q,
+                         float *const *recv_s);
+
+/* Quantize one token row (H channels) to q[H] and s[H/128]. */
+void oracle_quantize_row(int H, const uint16_t *xrow, uint8_t *q, float *s);
+
+/* Un-permute: u[p][:] = recv_y[r(p)][row(p)][:], u is [P,H] in (t,j) order
+ * ([torchtitan PR]: the token unpermute after the experts). */
+void oracle_unpermute(int T, int H, int k, int E, int R, const int32_t *idx,
+                      const int32_t *slot, const int32_t *roff,
+                      const uint16_t *const *recv_y, uint16_t *u);
+
+/* Weighted combine ([Perplexity blog], "Sérfræðinga-samsíðun": the routed
+ * results are weighted and summed; [DeepEP overview], "Pola penggunaan...":
+ * combine reduces expert outputs back to the source).  fp32 accumulation in
+ * ascending j with a correctly rounded fused multiply-add, then bf16 RNE.
+ * w == NULL means unit weights. */
+void oracle_combine(int T, int H, int k, int E, int R, const int32_t *idx,
+                    const int32_t *slot, const int32_t *roff,
+                    const uint16_t *const *recv_y, const float *w, uint16_t *out);
+
+/* Codecs. */
+uint8_t  oracle_e4m3_encode(float v);
+float    oracle_e4m3_decode(uint8_t c);
+uint16_t oracle_bf16_rne(float v);
+float    oracle_bf16_to_f32(uint16_t b);
+void     oracle_e4m3_encode_n(const float *v, uint8_t *out, int64_t n);
+void     oracle_e4m3_decode_n(const uint8_t *c, float *out, int64_t n);
+void     oracle_bf16_rne_n(const float *v, uint16_t *out, int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
