@@ -1,0 +1,281 @@
+"""Benchmark of the MoE dispatch / combine hot path on one MI355X.
+
+One step = ep_layout + ep_dispatch + ep_combine over one batch of the seeded
+synthetic workload (default: the V3-shaped headline, T=8192 tokens, hidden
+7168, top-8 of 256 experts over 8 simulated ranks, FP8 E4M3 dispatch with
+per-128-channel fp32 scales, BF16 combine).  Inputs are resident in HBM before
+the timed region; the expert stand-in (seeded bf16 rows in the receive
+buffers) is outside the path and is not timed.
+
+Prints ONE JSON line (rank 0, N=1):
+  value        = algorithmic bytes of a step / wall time of a step  [GB/s]
+  ms_per_step  = wall time over the K timed steps / K
+  roofline     = the dominant kernel (combine): algorithmic bytes per launch /
+                 its mean HIP-event duration, against 8 TB/s HBM peak
+  cpu_baseline = the CPU oracle (single thread) on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "dispatch+combine µs and achieved HBM GB/s at 8K tok, h7168, top-8, 1 GPU"
+
+
+def algorithmic_bytes(T, H, k, E, R, fp8):
+    """Bytes the method must move (reads of x / y / indices / weights, writes
+    of rows / scales / output / handle), per call."""
+    P = T * k
+    nb = H // 128
+    layout = 4 * P + 8 * P + 4 * (2 * E + 2 * R + 3)   # read idx, write slot/src, counts/offsets
+    if fp8:
+        dispatch = 2 * H * T + P * (H + 4 * nb) + 8 * P  # read x, write q + scales, read idx + slot
+    else:
+        dispatch = 2 * H * T + P * 2 * H + 8 * P
+    combine = 2 * H * P + 2 * H * T + 12 * P           # read y, write out, read w + idx + slot
+    return dict(layout=layout, dispatch=dispatch, combine=combine)
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def kernel_sources():
+    c = os.path.join(ROOT, "combine_ep_layout_03_amd", "csrc")
+    return {"combine": [os.path.join(c, "ep_combine.hip"), os.path.join(c, "ep_internal.h")],
+            "dispatch": [os.path.join(c, "ep_dispatch.hip"), os.path.join(c, "ep_internal.h")]}
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != source_sha(kernel_sources()[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(workload_name, sample_tokens, min_seconds):
+    """Time the CPU oracle (single thread) on the first `sample_tokens` tokens of
+    the workload, repeated until min_seconds of work; GB/s of algorithmic
+    bytes."""
+    import numpy as np
+    import oracle
+    from workloads import make_workload, make_expert_rows
+
+    w = make_workload(workload_name)
+    Ts = min(sample_tokens, w.T)
+    x, idx, wt = w.x[:Ts].copy(), w.topk_idx[:Ts].copy(), w.topk_w[:Ts].copy()
+    L0 = oracle.layout(idx, w.E, w.R)
+    y = make_expert_rows(Ts * w.k, w.H)
+    ys = [y[L0.rank_offsets[r]:L0.rank_offsets[r + 1]] for r in range(w.R)]
+    oracle.lib()
+    times = []
+    t_end = time.perf_counter() + min_seconds
+    while len(times) < 2 or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        L = oracle.layout(idx, w.E, w.R)
+        if w.fp8:
+            oracle.dispatch_fp8(x, idx, L)
+        else:
+            oracle.dispatch_bf16(x, idx, L)
+        oracle.combine(ys, idx, L, wt)
+        times.append(time.perf_counter() - t0)
+    b = algorithmic_bytes(Ts, w.H, w.k, w.E, w.R, w.fp8)
+    step_bytes = sum(b.values())
+    mean = statistics.mean(times)
+    return {"value": round(step_bytes / mean / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{workload_name} workload, first {Ts} of {w.T} tokens (layout + dispatch + "
+                      f"combine), {len(times)} repetitions, mean {mean:.3f} s each, single thread "
+                      f"of {os.cpu_count()} host cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="v3")
+    ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU-oracle baseline")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--num-workgroups", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the expert-parallel ranks are simulated as "
+              "destination buffers in one HBM, so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from combine_ep_layout_03_amd import build as epbuild
+    if not os.path.exists(epbuild.LIB):
+        epbuild.build()
+    import combine_ep_layout_03_amd as ep
+    from combine_ep_layout_03_amd import _lib
+    from combine_ep_layout_03_amd.buffers import Handle, RecvBuffers, alloc_workspace
+    from workloads import CONFIGS, make_workload
+
+    L = ep.load()
+    dev = "cuda"
+    w = make_workload(args.config)
+    cfg = ep.Config(w.T, w.H, w.k, w.E, w.R, fp8=w.fp8, num_workgroups=args.num_workgroups)
+    cap = ep.ep_recv_capacity_rows(cfg)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
+    idx, x, wts = up(w.topk_idx), up(w.x), up(w.topk_w)
+    h = Handle.alloc(cfg, dev)
+    ws = alloc_workspace(cfg, dev)
+    recv = RecvBuffers.alloc(cfg, cap, device=dev)
+    out = torch.empty((w.T, w.H), dtype=torch.int16, device=dev)
+
+    # layout once to size the expert stand-in rows: seeded N(0,1) bf16 rows in
+    # the valid part of each rank buffer
+    ep.ep_layout(cfg, idx, h, ws)
+    torch.cuda.synchronize()
+    rank_counts = h.rank_counts.cpu().tolist()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    ybufs = []
+    for r in range(w.R):
+        b = torch.zeros((cap, w.H), dtype=torch.int16, device=dev)
+        n = rank_counts[r]
+        if n:
+            b[:n] = torch.randn((n, w.H), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+        ybufs.append(b)
+    torch.cuda.synchronize()
+
+    # prebuilt C arguments for the timed loop (no per-call marshalling)
+    ccfg = cfg.c()
+    ch = _lib.ep_layout_t(*[getattr(h, n).data_ptr() for n, _ in _lib.ep_layout_t._fields_])
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    rx = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in recv.x])
+    rs = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in recv.scales]) if recv.scales else None
+    ry = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in ybufs])
+    pc, ph = ctypes.byref(ccfg), ctypes.byref(ch)
+
+    def layout():
+        st = L.ep_layout(pc, idx.data_ptr(), ph, ws.data_ptr(), sp)
+        assert st == 0, st
+
+    def dispatch():
+        st = L.ep_dispatch(pc, ph, idx.data_ptr(), x.data_ptr(), rx, rs, cap, sp)
+        assert st == 0, st
+
+    def combine():
+        st = L.ep_combine(pc, ph, idx.data_ptr(), ry, wts.data_ptr(), out.data_ptr(), cap, sp)
+        assert st == 0, st
+
+    # plain copy ceiling (1 GiB read + 1 GiB write), same run
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cms = []
+    for _ in range(5):
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        cms.append(e0.elapsed_time(e1))
+    copy_gbps = 2 * src.numel() / (statistics.median(cms) * 1e-3) / 1e9
+    del src, dst
+
+    for _ in range(args.warmup):
+        layout(); dispatch(); combine()
+    torch.cuda.synchronize()
+    assert int(h.error_flag.item()) == 0
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = ev[i]
+        e[0].record(stream)
+        layout()
+        e[1].record(stream)
+        dispatch()
+        e[2].record(stream)
+        combine()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(h.error_flag.item()) == 0
+
+    lay = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+    dis = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    com = [e[2].elapsed_time(e[3]) * 1e3 for e in ev]
+    dc = [a + b for a, b in zip(dis, com)]
+    b = algorithmic_bytes(w.T, w.H, w.k, w.E, w.R, w.fp8)
+    step_bytes = sum(b.values())
+    ms_per_step = wall / K * 1e3
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    mean_com = statistics.mean(com)
+    achieved = b["combine"] / (mean_com * 1e-6) / 1e9
+
+    def pct(v, q):
+        s = sorted(v)
+        return round(s[min(len(s) - 1, int(q * len(s)))], 2)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded: x ~ N(0,1) bf16, router logits N(0,1); expert outputs N(0,1) bf16)",
+        "config": {"workload": args.config, "T": w.T, "hidden": w.H, "top_k": w.k,
+                   "experts": w.E, "ranks": w.R,
+                   "dispatch": "fp8_e4m3 + fp32 per-128 scales" if w.fp8 else "bf16",
+                   "combine": "bf16 (fp32 accumulate)", "parallelism": "1 GPU, ranks simulated"},
+        "roofline": {"bound": "hbm", "kernel": "combine", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": load_traffic("combine", args.config),
+                     "algorithmic_bytes_per_launch": b["combine"], "mean_launch_us": round(mean_com, 2)},
+        "layout_us": round(statistics.median(lay), 2),
+        "dispatch_us": round(statistics.median(dis), 2),
+        "combine_us": round(statistics.median(com), 2),
+        "dc_us": round(statistics.median(dc), 2),
+        "dc_us_p10_p90": [pct(dc, 0.1), pct(dc, 0.9)],
+        "dc_GBps": round((b["dispatch"] + b["combine"]) / (statistics.median(dc) * 1e-6) / 1e9, 1),
+        "dispatch_GBps": round(b["dispatch"] / (statistics.median(dis) * 1e-6) / 1e9, 1),
+        "combine_GBps": round(b["combine"] / (statistics.median(com) * 1e-6) / 1e9, 1),
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "bytes_per_step": step_bytes,
+        "cpu_baseline": None,
+    }
+    if not args.skip_cpu:
+        res["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample_tokens, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

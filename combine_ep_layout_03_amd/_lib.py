@@ -1,0 +1,173 @@
+"""ctypes binding of libep.so (include/ep.h).  Argument marshalling only: every
+step of layout, dispatch, un-permute and combine runs in the library's HIP
+kernels.  Torch tensors supply device memory and the stream.
+
+The functions carry the C names: ep_layout, ep_dispatch, ep_combine,
+ep_unpermute, ep_recv_capacity_rows, ep_layout_workspace_bytes,
+ep_abi_version, ep_status_string.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libep.so")
+
+EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_CAPACITY, EP_ERR_HIP = 0, 1, 2, 3, 4
+EP_DEVERR_INDEX, EP_DEVERR_ROW, EP_DEVERR_INTERNAL = 1, 2, 4
+EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3 = 0, 1
+EP_MAX_RANKS, EP_MAX_TOPK, EP_MAX_EXPERTS, EP_MAX_HIDDEN = 64, 32, 2048, 65536
+
+# Every symbol include/ep.h declares.
+EXPORTS = ("ep_abi_version", "ep_status_string", "ep_recv_capacity_rows",
+           "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine",
+           "ep_unpermute")
+
+
+class EpError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (status %d)" % (what, ep_status_string(status), status))
+        self.status = status
+
+
+class ep_config(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("num_topk", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("num_ranks", ctypes.c_int32), ("dispatch_dtype", ctypes.c_int32),
+                ("num_workgroups", ctypes.c_int32)]
+
+
+class ep_layout_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("expert_counts", "expert_offsets", "rank_counts",
+                                               "rank_offsets", "slot_of", "src_of", "error_flag")]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libep.so.  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libep.so is not built (%s); run __graft_entry__.build() or "
+                           "python combine_ep_layout_03_amd/build.py" % path)
+    L = ctypes.CDLL(path)
+    vp, i64, cfgp, hp = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ep_config), ctypes.POINTER(ep_layout_t)
+    L.ep_abi_version.restype = ctypes.c_uint32
+    L.ep_abi_version.argtypes = []
+    L.ep_status_string.restype = ctypes.c_char_p
+    L.ep_status_string.argtypes = [ctypes.c_int32]
+    L.ep_recv_capacity_rows.restype = i64
+    L.ep_recv_capacity_rows.argtypes = [cfgp]
+    L.ep_layout_workspace_bytes.restype = ctypes.c_size_t
+    L.ep_layout_workspace_bytes.argtypes = [cfgp]
+    L.ep_layout.restype = ctypes.c_int32
+    L.ep_layout.argtypes = [cfgp, vp, hp, vp, vp]
+    L.ep_dispatch.restype = ctypes.c_int32
+    L.ep_dispatch.argtypes = [cfgp, hp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, vp]
+    L.ep_combine.restype = ctypes.c_int32
+    L.ep_combine.argtypes = [cfgp, hp, vp, ctypes.POINTER(vp), vp, vp, i64, vp]
+    L.ep_unpermute.restype = ctypes.c_int32
+    L.ep_unpermute.argtypes = [cfgp, hp, vp, ctypes.POINTER(vp), vp, i64, vp]
+    _lib = L
+    return L
+
+
+@dataclass
+class Config:
+    num_tokens: int
+    hidden: int
+    num_topk: int
+    num_experts: int
+    num_ranks: int
+    fp8: bool = False
+    num_workgroups: int = 0
+
+    def c(self) -> ep_config:
+        return ep_config(self.num_tokens, self.hidden, self.num_topk, self.num_experts,
+                         self.num_ranks, EP_DTYPE_FP8_E4M3 if self.fp8 else EP_DTYPE_BF16,
+                         self.num_workgroups)
+
+
+def _cfg(cfg) -> ep_config:
+    return cfg.c() if isinstance(cfg, Config) else cfg
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptrs(ts) -> ctypes.Array:
+    return (ctypes.c_void_p * len(ts))(*[_ptr(t) for t in ts])
+
+
+def _check(status: int, what: str) -> None:
+    if status != EP_OK:
+        raise EpError(status, what)
+
+
+def ep_abi_version() -> int:
+    return int(load().ep_abi_version())
+
+
+def ep_status_string(status: int) -> str:
+    return load().ep_status_string(int(status)).decode()
+
+
+def ep_recv_capacity_rows(cfg) -> int:
+    return int(load().ep_recv_capacity_rows(ctypes.byref(_cfg(cfg))))
+
+
+def ep_layout_workspace_bytes(cfg) -> int:
+    return int(load().ep_layout_workspace_bytes(ctypes.byref(_cfg(cfg))))
+
+
+def _handle(h) -> ep_layout_t:
+    if isinstance(h, ep_layout_t):
+        return h
+    return ep_layout_t(*[_ptr(getattr(h, n)) for n, _ in ep_layout_t._fields_])
+
+
+def ep_layout(cfg, topk_idx, handle, workspace, stream=None) -> None:
+    _check(load().ep_layout(ctypes.byref(_cfg(cfg)), _ptr(topk_idx), ctypes.byref(_handle(handle)),
+                            _ptr(workspace), _stream(stream)), "ep_layout")
+
+
+def ep_dispatch(cfg, handle, topk_idx, x, recv_x, recv_scales, capacity_rows, stream=None) -> None:
+    rs = None if recv_scales is None else _ptrs(recv_scales)
+    _check(load().ep_dispatch(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)), _ptr(topk_idx),
+                              _ptr(x), _ptrs(recv_x), rs, int(capacity_rows), _stream(stream)),
+           "ep_dispatch")
+
+
+def ep_combine(cfg, handle, topk_idx, recv_y, topk_weights, out, capacity_rows, stream=None) -> None:
+    _check(load().ep_combine(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)), _ptr(topk_idx),
+                             _ptrs(recv_y), _ptr(topk_weights), _ptr(out), int(capacity_rows),
+                             _stream(stream)), "ep_combine")
+
+
+def ep_unpermute(cfg, handle, topk_idx, recv_y, out, capacity_rows, stream=None) -> None:
+    _check(load().ep_unpermute(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)), _ptr(topk_idx),
+                               _ptrs(recv_y), _ptr(out), int(capacity_rows), _stream(stream)),
+           "ep_unpermute")

@@ -1,0 +1,146 @@
+// ep_api.cpp -- the C ABI declared in include/ep.h: host-side validation,
+// launch planning and status mapping.  Every check here is synchronous and
+// enqueues nothing when it fails; the kernels are in ep_layout.hip,
+// ep_dispatch.hip and ep_combine.hip.
+#include <cstdio>
+#include <cstdlib>
+
+#include "ep_internal.h"
+
+namespace {
+
+bool debug_enabled() {
+  const char *v = std::getenv("EP_DEBUG");
+  return v && v[0] && v[0] != '0';
+}
+
+bool config_ok(const ep_config *c) {
+  if (!c) return false;
+  if (c->num_tokens < 1 || c->num_topk < 1 || c->num_topk > EP_MAX_TOPK) return false;
+  if (c->num_experts < 1 || c->num_experts > EP_MAX_EXPERTS) return false;
+  if (c->num_ranks < 1 || c->num_ranks > EP_MAX_RANKS) return false;
+  if (c->num_experts % c->num_ranks != 0) return false;
+  if (c->hidden < 8 || c->hidden > EP_MAX_HIDDEN || c->hidden % 8 != 0) return false;
+  if (c->dispatch_dtype != EP_DTYPE_BF16 && c->dispatch_dtype != EP_DTYPE_FP8_E4M3) return false;
+  if (c->dispatch_dtype == EP_DTYPE_FP8_E4M3 && c->hidden % 128 != 0) return false;
+  if (c->num_workgroups < 0) return false;
+  if ((int64_t)c->num_tokens * c->num_topk > INT32_MAX) return false;
+  return true;
+}
+
+bool handle_ok(const ep_layout_t *h) {
+  return h && h->expert_counts && h->expert_offsets && h->rank_counts && h->rank_offsets &&
+         h->slot_of && h->src_of && h->error_flag;
+}
+
+ep_status from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+void trace(const char *what, const ep_config *c, int grid) {
+  if (!debug_enabled()) return;
+  std::fprintf(stderr,
+               "[ep] %s T=%d H=%d k=%d E=%d R=%d dtype=%d grid=%d block=%d\n", what,
+               c->num_tokens, c->hidden, c->num_topk, c->num_experts, c->num_ranks,
+               c->dispatch_dtype, grid, ep::kRowWaves * ep::kWave);
+}
+
+// Shared checks of dispatch / combine / unpermute.
+ep_status row_call_ok(const ep_config *cfg, const ep_layout_t *h, const int32_t *topk_idx,
+                      int64_t capacity_rows) {
+  if (!config_ok(cfg) || !handle_ok(h) || !topk_idx) return EP_ERR_INVALID_ARG;
+  if (capacity_rows < (int64_t)cfg->num_tokens * cfg->num_topk) return EP_ERR_CAPACITY;
+  return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t ep_abi_version(void) { return EP_ABI_VERSION; }
+
+const char *ep_status_string(ep_status status) {
+  switch (status) {
+    case EP_OK: return "ok";
+    case EP_ERR_INVALID_ARG: return "invalid argument";
+    case EP_ERR_UNSUPPORTED: return "unsupported";
+    case EP_ERR_CAPACITY: return "receive capacity below ep_recv_capacity_rows()";
+    case EP_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t ep_recv_capacity_rows(const ep_config *cfg) {
+  if (!config_ok(cfg)) return -1;
+  return (int64_t)cfg->num_tokens * cfg->num_topk;
+}
+
+size_t ep_layout_workspace_bytes(const ep_config *cfg) {
+  if (!config_ok(cfg)) return 0;
+  return ep::plan_layout((int64_t)cfg->num_tokens * cfg->num_topk, cfg->num_experts)
+      .workspace_bytes;
+}
+
+ep_status ep_layout(const ep_config *cfg, const int32_t *topk_idx, const ep_layout_t *h,
+                    void *workspace, hipStream_t stream) {
+  if (!config_ok(cfg) || !handle_ok(h) || !topk_idx || !workspace) return EP_ERR_INVALID_ARG;
+  const ep::LayoutPlan plan =
+      ep::plan_layout((int64_t)cfg->num_tokens * cfg->num_topk, cfg->num_experts);
+  if (debug_enabled())
+    std::fprintf(stderr, "[ep] layout P=%lld chunks=%d x %d pairs, workgroups=%d\n",
+                 (long long)plan.P, plan.C, plan.S, plan.workgroups);
+  return from_hip(ep::launch_layout(*cfg, plan, topk_idx, *h, workspace, stream));
+}
+
+ep_status ep_dispatch(const ep_config *cfg, const ep_layout_t *h, const int32_t *topk_idx,
+                      const void *x, void *const *recv_x, float *const *recv_scales,
+                      int64_t capacity_rows, hipStream_t stream) {
+  ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
+  if (st != EP_OK) return st;
+  if (!x || !recv_x) return EP_ERR_INVALID_ARG;
+  const bool fp8 = cfg->dispatch_dtype == EP_DTYPE_FP8_E4M3;
+  if (fp8 && !recv_scales) return EP_ERR_INVALID_ARG;
+  ep::RankPtrs rx{};
+  ep::ScalePtrs rs{};
+  for (int r = 0; r < cfg->num_ranks; ++r) {
+    if (!recv_x[r]) return EP_ERR_INVALID_ARG;
+    rx.p[r] = recv_x[r];
+    if (fp8) {
+      if (!recv_scales[r]) return EP_ERR_INVALID_ARG;
+      rs.p[r] = recv_scales[r];
+    }
+  }
+  trace("dispatch", cfg, ep::row_grid(*cfg, cfg->num_tokens));
+  return from_hip(ep::launch_dispatch(*cfg, *h, topk_idx, x, rx, rs, capacity_rows, stream));
+}
+
+ep_status ep_combine(const ep_config *cfg, const ep_layout_t *h, const int32_t *topk_idx,
+                     const void *const *recv_y, const float *topk_weights, void *out,
+                     int64_t capacity_rows, hipStream_t stream) {
+  ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
+  if (st != EP_OK) return st;
+  if (!recv_y || !out) return EP_ERR_INVALID_ARG;
+  ep::RankCPtrs ry{};
+  for (int r = 0; r < cfg->num_ranks; ++r) {
+    if (!recv_y[r]) return EP_ERR_INVALID_ARG;
+    ry.p[r] = recv_y[r];
+  }
+  trace("combine", cfg, ep::row_grid(*cfg, cfg->num_tokens));
+  return from_hip(
+      ep::launch_combine(*cfg, *h, topk_idx, ry, topk_weights, out, capacity_rows, stream));
+}
+
+ep_status ep_unpermute(const ep_config *cfg, const ep_layout_t *h, const int32_t *topk_idx,
+                       const void *const *recv_y, void *out, int64_t capacity_rows,
+                       hipStream_t stream) {
+  ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
+  if (st != EP_OK) return st;
+  if (!recv_y || !out) return EP_ERR_INVALID_ARG;
+  ep::RankCPtrs ry{};
+  for (int r = 0; r < cfg->num_ranks; ++r) {
+    if (!recv_y[r]) return EP_ERR_INVALID_ARG;
+    ry.p[r] = recv_y[r];
+  }
+  trace("unpermute", cfg, ep::row_grid(*cfg, (int64_t)cfg->num_tokens * cfg->num_topk));
+  return from_hip(ep::launch_unpermute(*cfg, *h, topk_idx, ry, out, capacity_rows, stream));
+}
+
+}  // extern "C"

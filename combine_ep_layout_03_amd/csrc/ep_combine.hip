@@ -1,0 +1,153 @@
+// ep_combine.hip -- combine and un-permute on gfx950.
+//
+// Pages: [Perplexity blog] "Lower latency and higher throughput with
+// multi-node DeepSeek deployment", "Sérfræðinga-samsíðun" (each token's 8
+// routed results are weighted and summed) and "Skörun" (combine was the
+// largest communication item: 1012 us before micro-batching);
+// [DeepEP overview] "DeepSeek merilis library open source DeepEP ...",
+// "Pola penggunaan ..." (combine reduces expert outputs back to the source
+// rank; the backward of dispatch is a combine) and "Hasil pengukuran
+// performa" (BF16 combine); [torchtitan PR] "Integrate DeepEP to experimental
+// torchtitan" (the token unpermute after the experts).
+//
+// Design: one wavefront per output token (grid-stride).  Lanes 0..k-1 resolve
+// the token's k received rows and weights; each lane then owns 8 channels
+// (16 B) per step, issues the k gathered 16-byte loads of a step before any
+// arithmetic (up to 8 rows in flight per lane), and folds them in ascending j
+// with fp32 fused multiply-adds from +0.  Each output element is written once
+// (16-byte stores, bf16 nearest-even); there are no atomics.  The un-permute
+// is fused into the loads; ep_unpermute exposes it on its own for tests.
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+constexpr int kThreads = kRowWaves * kWave;
+constexpr int kJB = 8;  // rows whose loads are issued together
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// binary32 -> bf16 bits, nearest with ties to even; NaN stays a quiet NaN.
+__device__ inline uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Lane j < k: byte address of pair (t, j)'s received row (0 if unusable,
+// which raises EP_DEVERR_ROW).
+__device__ inline uint64_t src_row(const int32_t *__restrict__ idx,
+                                   const int32_t *__restrict__ slot_of,
+                                   const int32_t *__restrict__ rank_offsets,
+                                   int32_t *__restrict__ err, int64_t p, int32_t E, int32_t El,
+                                   int64_t cap, const RankCPtrs &ry, int64_t rowbytes) {
+  const int32_t e = idx[p];
+  if ((uint32_t)e < (uint32_t)E) {
+    const int32_t r = e / El;
+    const int64_t rr = (int64_t)slot_of[p] - rank_offsets[r];
+    if (rr >= 0 && rr < cap) return (uint64_t)ry.p[r] + (uint64_t)(rr * rowbytes);
+  }
+  atomicOr(err, (int32_t)EP_DEVERR_ROW);
+  return 0;
+}
+
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ slot_of,
+    const int32_t *__restrict__ rank_offsets, int32_t *__restrict__ err,
+    const float *__restrict__ w, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El,
+    int64_t cap, RankCPtrs ry, uint16_t *__restrict__ out) {
+  if (*err != 0) return;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int nch = H / 8;
+  for (int64_t t = (int64_t)blockIdx.x * kRowWaves + wave; t < T;
+       t += (int64_t)gridDim.x * kRowWaves) {
+    uint64_t src = 0;
+    float wj = 0.0f;
+    if (lane < k) {
+      src = src_row(idx, slot_of, rank_offsets, err, t * k + lane, E, El, cap, ry, (int64_t)H * 2);
+      wj = w ? w[t * k + lane] : 1.0f;
+    }
+    if (__ballot(lane < k && src == 0) != 0) continue;  // a bad row: write nothing for t
+    u32x4 *orow = reinterpret_cast<u32x4 *>(out + t * H);
+    for (int c = lane; c < nch; c += kWave) {
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+      for (int j0 = 0; j0 < k; j0 += kJB) {
+        u32x4 v[kJB];
+#pragma unroll
+        for (int jj = 0; jj < kJB; ++jj) {
+          if (j0 + jj < k) {
+            const u32x4 *yrow = reinterpret_cast<const u32x4 *>(readlane64(src, j0 + jj));
+            v[jj] = __builtin_nontemporal_load(yrow + c);
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < kJB; ++jj) {
+          if (j0 + jj < k) {
+            const float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j0 + jj));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc[2 * i] = __builtin_fmaf(wv, __uint_as_float(v[jj][i] << 16), acc[2 * i]);
+              acc[2 * i + 1] = __builtin_fmaf(wv, __uint_as_float(v[jj][i] & 0xFFFF0000u), acc[2 * i + 1]);
+            }
+          }
+        }
+      }
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = bf16_bits(acc[2 * i]) | (bf16_bits(acc[2 * i + 1]) << 16);
+      __builtin_nontemporal_store(o, orow + c);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void unpermute_kernel(
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ slot_of,
+    const int32_t *__restrict__ rank_offsets, int32_t *__restrict__ err, int64_t P, int32_t H,
+    int32_t E, int32_t El, int64_t cap, RankCPtrs ry, uint16_t *__restrict__ out) {
+  if (*err != 0) return;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int nch = H / 8;
+  for (int64_t p = (int64_t)blockIdx.x * kRowWaves + wave; p < P;
+       p += (int64_t)gridDim.x * kRowWaves) {
+    uint64_t src = 0;
+    if (lane == 0) src = src_row(idx, slot_of, rank_offsets, err, p, E, El, cap, ry, (int64_t)H * 2);
+    src = readlane64(src, 0);
+    if (src == 0) continue;
+    const u32x4 *yrow = reinterpret_cast<const u32x4 *>(src);
+    u32x4 *orow = reinterpret_cast<u32x4 *>(out + p * H);
+    for (int c = lane; c < nch; c += kWave) orow[c] = yrow[c];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
+                          const RankCPtrs &ry, const float *w, void *out, int64_t capacity_rows,
+                          hipStream_t s) {
+  const int grid = row_grid(c, c.num_tokens);
+  hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kThreads), 0, s, topk_idx, h.slot_of,
+                     h.rank_offsets, h.error_flag, w, c.num_tokens, c.hidden, c.num_topk,
+                     c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,
+                     static_cast<uint16_t *>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
+                            const RankCPtrs &ry, void *out, int64_t capacity_rows, hipStream_t s) {
+  const int64_t P = (int64_t)c.num_tokens * c.num_topk;
+  const int grid = row_grid(c, P);
+  hipLaunchKernelGGL(unpermute_kernel, dim3(grid), dim3(kThreads), 0, s, topk_idx, h.slot_of,
+                     h.rank_offsets, h.error_flag, P, c.hidden, c.num_experts,
+                     c.num_experts / c.num_ranks, capacity_rows, ry,
+                     static_cast<uint16_t *>(out));
+  return hipGetLastError();
+}
+
+}  // namespace ep

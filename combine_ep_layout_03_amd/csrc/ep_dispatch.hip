@@ -1,0 +1,202 @@
+// ep_dispatch.hip -- dispatch on gfx950: gather every token row into the
+// receive buffers of its k experts' ranks, optionally quantized to FP8.
+//
+// Pages: [DeepEP overview] "DeepSeek merilis library open source DeepEP ...",
+// "Pola penggunaan ..." (dispatch routes tokens to the experts' ranks, from
+// BF16 or FP8) and "Hasil pengukuran performa" (the V3 config: FP8 dispatch);
+// [Perplexity blog] "Lower latency and higher throughput with multi-node
+// DeepSeek deployment", "Magntölun" (activation scales over 128-element
+// vectors, computed on the fly; the horizontal amax is the awkward part).
+//
+// Design: one wavefront per token (grid-stride over tokens).  The token row
+// is read once; FP8 quantization is done once per token, and the k copies are
+// written with 16-byte non-temporal stores (rows are streamed out, never
+// re-read by this kernel).  Lanes 0..k-1 resolve the k destination rows; the
+// row base addresses are then taken with readlane, so every copy is a
+// scalar-base + vector-offset store.
+//   BF16: lane = 8 channels (16 B).
+//   FP8:  lane = 16 channels (2 x 16 B of bf16 -> 16 B of E4M3); 8 lanes form
+//         one 128-channel block, so a wave covers 8 blocks per step and the
+//         block amax is 3 xor-shuffles.  amax is taken on the bf16 bit
+//         patterns (|x| is monotone in its low 15 bits), the scale is the
+//         correctly rounded binary32 a/448 and every code is E4M3 of the
+//         correctly rounded binary32 quotient x/s.
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+constexpr int kThreads = kRowWaves * kWave;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// OCP E4M3 ("fn") of a binary32 value, nearest-even, saturating at 448.
+// Normal results: round the binary32 significand to 3 bits on the bit
+// pattern and rebias the exponent (127 -> 7).  Below 2^-6 the E4M3 spacing is
+// 2^-9, so the code is rint(|v| * 2^9) (the scaling is exact).
+__device__ inline uint32_t e4m3_code(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x43E00000u)  // |v| >= 448 (NaN is never produced here)
+    return sign | (a > 0x7F800000u ? 0x7Fu : 0x7Eu);
+  if (a < 0x3C800000u)   // |v| < 2^-6
+    return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;  // exp8 | mant3, rounded
+  const uint32_t code = r - (120u << 3);
+  return sign | (code < 0x7Eu ? code : 0x7Eu);
+}
+
+__device__ inline uint32_t bf16_absbits_max(u32x4 v, uint32_t m) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = v[i] & 0x7FFFu, hi = (v[i] >> 16) & 0x7FFFu;
+    m = lo > m ? lo : m;
+    m = hi > m ? hi : m;
+  }
+  return m;
+}
+
+// 4 bf16 pairs -> 8 E4M3 codes (2 dwords), each code of (x / s).
+__device__ inline void quant8(u32x4 v, float s, bool zero, uint32_t &w0, uint32_t &w1) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16);
+    const float hi = __uint_as_float(v[i] & 0xFFFF0000u);
+    c[2 * i] = zero ? 0u : e4m3_code(lo / s);
+    c[2 * i + 1] = zero ? 0u : e4m3_code(hi / s);
+  }
+  w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+}
+
+// Lane j < k: byte address of token t's destination row j (0 if unusable,
+// which also raises EP_DEVERR_ROW).  `rowbytes` is the destination row pitch.
+__device__ inline uint64_t dest_row(const int32_t *__restrict__ idx,
+                                    const int32_t *__restrict__ slot_of,
+                                    const int32_t *__restrict__ rank_offsets,
+                                    int32_t *__restrict__ err, int64_t p, int32_t E, int32_t El,
+                                    int64_t cap, const void *const *base, int64_t rowbytes,
+                                    int32_t &rank, int64_t &row) {
+  const int32_t e = idx[p];
+  if ((uint32_t)e < (uint32_t)E) {
+    const int32_t r = e / El;
+    const int64_t rr = (int64_t)slot_of[p] - rank_offsets[r];
+    if (rr >= 0 && rr < cap) {
+      rank = r;
+      row = rr;
+      return (uint64_t)base[r] + (uint64_t)(rr * rowbytes);
+    }
+  }
+  atomicOr(err, (int32_t)EP_DEVERR_ROW);
+  return 0;
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ slot_of, const int32_t *__restrict__ rank_offsets,
+    int32_t *__restrict__ err, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El, int64_t cap,
+    RankPtrs rx) {
+  if (*err != 0) return;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int nch = H / 8;  // 16-byte chunks per row
+  for (int64_t t = (int64_t)blockIdx.x * kRowWaves + wave; t < T;
+       t += (int64_t)gridDim.x * kRowWaves) {
+    uint64_t dst = 0;
+    if (lane < k) {
+      int32_t r;
+      int64_t row;
+      dst = dest_row(idx, slot_of, rank_offsets, err, t * k + lane, E, El, cap,
+                     (const void *const *)rx.p, (int64_t)H * 2, r, row);
+    }
+    if (__ballot(lane < k && dst == 0) != 0) continue;  // a bad row: write nothing for t
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + t * H);
+    for (int c = lane; c < nch; c += kWave) {
+      const u32x4 v = __builtin_nontemporal_load(src + c);
+      for (int j = 0; j < k; ++j) {
+        u32x4 *d = reinterpret_cast<u32x4 *>(readlane64(dst, j));
+        __builtin_nontemporal_store(v, d + c);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ slot_of, const int32_t *__restrict__ rank_offsets,
+    int32_t *__restrict__ err, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El, int64_t cap,
+    RankPtrs rq, ScalePtrs rs) {
+  if (*err != 0) return;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int nb = H / 128;  // 128-channel blocks per row
+  for (int64_t t = (int64_t)blockIdx.x * kRowWaves + wave; t < T;
+       t += (int64_t)gridDim.x * kRowWaves) {
+    uint64_t qdst = 0, sdst = 0;
+    if (lane < k) {
+      int32_t r = 0;
+      int64_t row = 0;
+      qdst = dest_row(idx, slot_of, rank_offsets, err, t * k + lane, E, El, cap,
+                      (const void *const *)rq.p, (int64_t)H, r, row);
+      if (qdst) sdst = (uint64_t)(rs.p[r] + row * nb);
+    }
+    if (__ballot(lane < k && qdst == 0) != 0) continue;
+    const uint16_t *xrow = x + t * H;
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      const int blk = b0 + lane / 8;
+      const bool valid = blk < nb;
+      const int ch = blk * 128 + (lane % 8) * 16;
+      u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+      if (valid) {
+        v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch));
+        v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch + 8));
+      }
+      uint32_t m = bf16_absbits_max(v1, bf16_absbits_max(v0, 0u));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 4, kWave));
+      const bool zero = (m == 0u);
+      const float s = zero ? 0.0f : __uint_as_float(m << 16) / 448.0f;
+      uint32_t q0, q1, q2, q3;
+      quant8(v0, s, zero, q0, q1);
+      quant8(v1, s, zero, q2, q3);
+      const u32x4 q = {q0, q1, q2, q3};
+      for (int j = 0; j < k; ++j) {
+        uint8_t *d = reinterpret_cast<uint8_t *>(readlane64(qdst, j));
+        float *sd = reinterpret_cast<float *>(readlane64(sdst, j));
+        if (valid) {
+          __builtin_nontemporal_store(q, reinterpret_cast<u32x4 *>(d + ch));
+          if ((lane % 8) == 0) sd[blk] = s;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
+                           const void *x, const RankPtrs &rx, const ScalePtrs &rs,
+                           int64_t capacity_rows, hipStream_t s) {
+  const int grid = row_grid(c, c.num_tokens);
+  const int32_t El = c.num_experts / c.num_ranks;
+  if (c.dispatch_dtype == EP_DTYPE_FP8_E4M3) {
+    hipLaunchKernelGGL(dispatch_fp8_kernel, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const uint16_t *>(x), topk_idx, h.slot_of, h.rank_offsets,
+                       h.error_flag, c.num_tokens, c.hidden, c.num_topk, c.num_experts, El,
+                       capacity_rows, rx, rs);
+  } else {
+    hipLaunchKernelGGL(dispatch_bf16_kernel, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const uint16_t *>(x), topk_idx, h.slot_of, h.rank_offsets,
+                       h.error_flag, c.num_tokens, c.hidden, c.num_topk, c.num_experts, El,
+                       capacity_rows, rx);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ep

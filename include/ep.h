@@ -1,0 +1,191 @@
+/*
+ * ep.h -- C ABI of the MI355X (gfx950) MoE token dispatch / combine library.
+ *
+ * Pages cited (by title and section):
+ *   [DeepEP overview]  "DeepSeek merilis library open source DeepEP untuk
+ *                      pelatihan dan inferensi MoE" (GeekNews, Indonesian):
+ *                      "Antarmuka berpusat pada ElasticBuffer" (buffers sized
+ *                      from the MoE config, a size hint, SM counts computed
+ *                      analytically with a per-call override) and "Pola
+ *                      penggunaan untuk pelatihan, prefill, dan decoding"
+ *                      (dispatch routes tokens to their experts' ranks and
+ *                      returns a handle with per-expert token counts for the
+ *                      GEMM; combine reduces expert outputs back; the handle
+ *                      is reused while gating is unchanged; the backward of
+ *                      dispatch is a combine and vice versa).
+ *   [Perplexity blog]  "Lower latency and higher throughput with multi-node
+ *                      DeepSeek deployment" (Icelandic rendering):
+ *                      "Sérfræðinga-samsíðun" (each GPU holds 256/EP experts;
+ *                      the 8 routed results are weighted and summed),
+ *                      "Magntölun" (activation scales over 128-element
+ *                      vectors, computed on the fly, M x ceil_div(K,128)),
+ *                      "MoE-beirari" (dense dispatch/combine need routing
+ *                      summed per expert), "CUDA-graf" and the persistent-
+ *                      kernel paragraph of "Magntölun" (under graphs, kernels
+ *                      read the token counts on the device instead of sizing
+ *                      work from the upper-bound buffer).
+ *   [torchtitan PR]    "Integrate DeepEP to experimental torchtitan" (the
+ *                      token unpermute after the experts; index selection on
+ *                      the host costs CPU time).
+ *
+ * Model.  One GPU.  The R expert-parallel "ranks" are R destination buffers in
+ * the same HBM; rank r owns the experts [r*E/R, (r+1)*E/R).  A (token t, top-k
+ * slot j) pair p = t*k + j is one received row.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host).  All memory belongs
+ *     to the caller; the library allocates nothing, keeps no pointer after a
+ *     call returns and has no global mutable state, so calls on distinct
+ *     handles and streams are independent.
+ *   - Work is enqueued on `stream` and never synchronizes; inputs must stay
+ *     alive and unmodified until the stream has passed the call.  Every call
+ *     can be captured into a hipGraph (no host sync, no allocation, no memset
+ *     nodes).
+ *   - Host-checkable problems (NULL pointers, bad sizes, too small a
+ *     capacity) return a nonzero ep_status at once and enqueue nothing.
+ *   - Data problems found on the device (a routing index outside [0,E), a
+ *     row outside the capacity) set bits in the handle's error word; dispatch,
+ *     combine and unpermute read the word first and then write nothing.
+ *   - Output bytes do not depend on ep_config.num_workgroups.
+ *
+ * Data types: routing indices int32 [T,k] row-major; weights fp32 [T,k];
+ * activations bf16 as 16-bit patterns; FP8 is OCP E4M3 ("fn", max 448) one
+ * byte per channel; scales fp32.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EP_ABI_VERSION 1u
+
+/* Limits of this build. */
+#define EP_MAX_RANKS 64    /* R: per-rank buffer pointers travel as kernel arguments */
+#define EP_MAX_TOPK 32     /* k */
+#define EP_MAX_EXPERTS 2048 /* E: the layout keeps per-expert counters in LDS */
+#define EP_MAX_HIDDEN 65536 /* H */
+
+typedef int32_t ep_status;
+#define EP_OK 0
+#define EP_ERR_INVALID_ARG 1 /* NULL pointer or a size outside the limits */
+#define EP_ERR_UNSUPPORTED 2 /* a valid request this build does not implement */
+#define EP_ERR_CAPACITY 3    /* capacity_rows below ep_recv_capacity_rows() */
+#define EP_ERR_HIP 4         /* a HIP launch failed (hipGetLastError) */
+
+/* Bits of the device error word (ep_layout_t.error_flag[0]). */
+#define EP_DEVERR_INDEX 1u    /* ep_layout saw an index outside [0,E) */
+#define EP_DEVERR_ROW 2u      /* dispatch/combine saw a row outside [0,capacity) */
+#define EP_DEVERR_INTERNAL 4u /* ep_layout computed a slot outside [0,T*k): a library bug */
+
+typedef int32_t ep_dtype;
+#define EP_DTYPE_BF16 0     /* dispatch copies bf16 rows */
+#define EP_DTYPE_FP8_E4M3 1 /* dispatch quantizes rows to E4M3 + fp32 scales */
+
+typedef struct {
+  int32_t num_tokens;     /* T >= 1 (cf. num_max_tokens_per_rank of the buffer) */
+  int32_t hidden;         /* H, multiple of 8; of 128 under FP8 */
+  int32_t num_topk;       /* k in [1, EP_MAX_TOPK] */
+  int32_t num_experts;    /* E in [1, EP_MAX_EXPERTS], E % R == 0 */
+  int32_t num_ranks;      /* R in [1, EP_MAX_RANKS] */
+  int32_t dispatch_dtype; /* ep_dtype (cf. use_fp8_dispatch) */
+  int32_t num_workgroups; /* 0 = analytic default; otherwise the grid size of
+                             dispatch / combine / unpermute (cf. the per-call
+                             SM-count override) */
+} ep_config;
+
+/* The routing handle.  Caller-allocated device arrays; ep_layout fills them
+ * and dispatch / combine / unpermute read them.  Reusing one handle across
+ * calls with unchanged routing is the cached-handle path. */
+typedef struct {
+  int32_t *expert_counts;  /* [E]   rows routed to each expert */
+  int32_t *expert_offsets; /* [E+1] exclusive prefix of expert_counts (global slot space) */
+  int32_t *rank_counts;    /* [R]   rows valid in each rank buffer; sums to T*k */
+  int32_t *rank_offsets;   /* [R+1] = expert_offsets[r*E/R]; rank_offsets[R] = T*k */
+  int32_t *slot_of;        /* [T*k] pair p -> global slot; its row in rank r's
+                              buffer is slot_of[p] - rank_offsets[r] */
+  int32_t *src_of;         /* [T*k] global slot -> pair p (inverse of slot_of) */
+  int32_t *error_flag;     /* [1]   EP_DEVERR_* bits, 0 = ok */
+} ep_layout_t;
+
+/* EP_ABI_VERSION of the loaded library. */
+uint32_t ep_abi_version(void);
+
+/* Static text for a status code. */
+const char *ep_status_string(ep_status status);
+
+/* Rows each rank buffer must hold: T*k, the worst case (every pair of every
+ * token on one rank; a token may name one expert twice).  Cf. the buffer size
+ * hint of [DeepEP overview] "Antarmuka berpusat pada ElasticBuffer".
+ * Returns -1 for an invalid config. */
+int64_t ep_recv_capacity_rows(const ep_config *cfg /*(host)*/);
+
+/* Bytes of device workspace ep_layout needs for this config (its per-chunk
+ * expert histograms).  Returns 0 for an invalid config. */
+size_t ep_layout_workspace_bytes(const ep_config *cfg /*(host)*/);
+
+/* Routing layout ([Perplexity blog] "MoE-beirari"; [DeepEP overview] "Pola
+ * penggunaan ...").  From topk_idx [T,k] computes
+ *   expert_counts[e] = #{p : topk_idx[p] = e},
+ *   expert_offsets   = exclusive prefix over e,
+ *   rank_counts[r], rank_offsets[r] over rank r's experts,
+ *   slot_of[p] = expert_offsets[e] + #{p' < p : topk_idx[p'] = e}
+ *     (a counting sort by expert that keeps ascending p inside each expert:
+ *      the expert-contiguous "GEMM layout"), and src_of = slot_of^-1,
+ * and writes error_flag (EP_DEVERR_INDEX when an index is outside [0,E); the
+ * other handle arrays are then unspecified).  `workspace` must hold
+ * ep_layout_workspace_bytes(cfg) bytes; its contents on entry do not matter
+ * and are clobbered.  Launches two kernels on `stream`. */
+ep_status ep_layout(const ep_config *cfg /*(host)*/, const int32_t *topk_idx,
+                    const ep_layout_t *h /*(host struct of device pointers)*/,
+                    void *workspace, hipStream_t stream);
+
+/* Dispatch ([DeepEP overview] "Pola penggunaan ...": route each token to its
+ * top-k experts' ranks; [Perplexity blog] "Magntölun" for FP8).  For every
+ * pair p = (t, j), with r = topk_idx[p] / (E/R) and row = slot_of[p] -
+ * rank_offsets[r]:
+ *   BF16: recv_x[r] row `row` (H bf16) := x[t], bit for bit;
+ *   FP8:  for each 128-channel block b of x[t]: a = max|x|, s = a/448 (fp32,
+ *         correctly rounded), q = E4M3(x/s) (fp32 quotient, round to nearest
+ *         even, saturating at 448); a = 0 gives s = 0 and q = 0x00;
+ *         recv_x[r] row `row` (H bytes) := q, recv_scales[r] row `row`
+ *         (H/128 fp32) := s.  Every copy of a token is byte-identical.
+ * x is [T,H] bf16; recv_x / recv_scales are (host) arrays of R device
+ * pointers to row-major buffers of capacity_rows rows (recv_scales is ignored
+ * and may be NULL for BF16).  Rows past rank_counts[r] are not written. */
+ep_status ep_dispatch(const ep_config *cfg /*(host)*/, const ep_layout_t *h /*(host)*/,
+                      const int32_t *topk_idx, const void *x,
+                      void *const *recv_x /*(host)[R]*/, float *const *recv_scales /*(host)[R]*/,
+                      int64_t capacity_rows, hipStream_t stream);
+
+/* Combine ([Perplexity blog] "Sérfræðinga-samsíðun": the routed results are
+ * weighted and summed; [DeepEP overview] "Pola penggunaan ...": combine
+ * reduces expert outputs back to the source).  For every token t and channel
+ * h:  acc = +0;  for j = 0..k-1:  acc = fma(w[t][j], y_j[h], acc)  (fp32);
+ * out[t][h] = bf16(acc) rounded to nearest even, where y_j is row
+ * slot_of[t*k+j] - rank_offsets[r] of recv_y[r].  This fuses the un-permute.
+ * topk_weights NULL means all weights 1 (the backward of dispatch).
+ * recv_y is a (host) array of R device pointers to [capacity_rows, H] bf16;
+ * out is [T,H] bf16 and is written exactly once per element. */
+ep_status ep_combine(const ep_config *cfg /*(host)*/, const ep_layout_t *h /*(host)*/,
+                     const int32_t *topk_idx, const void *const *recv_y /*(host)[R]*/,
+                     const float *topk_weights, void *out, int64_t capacity_rows,
+                     hipStream_t stream);
+
+/* Un-permute ([torchtitan PR]: the token unpermute after the experts) as a
+ * standalone call for testing: out[p] (H bf16) := recv_y[r(p)] row row(p), so
+ * out is [T*k, H] in (t, j) order.  Same arguments and errors as ep_combine. */
+ep_status ep_unpermute(const ep_config *cfg /*(host)*/, const ep_layout_t *h /*(host)*/,
+                       const int32_t *topk_idx, const void *const *recv_y /*(host)[R]*/,
+                       void *out, int64_t capacity_rows, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EP_H */

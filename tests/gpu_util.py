@@ -1,0 +1,118 @@
+"""Helpers for the GPU tests: run the HIP path through the C ABI on seeded
+workloads and bring the results back as numpy arrays."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import combine_ep_layout_03_amd as ep
+from combine_ep_layout_03_amd.buffers import Handle, RecvBuffers, alloc_workspace
+
+DEV = "cuda"
+POISON = 0xAA
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def config_of(w, num_workgroups=0) -> ep.Config:
+    return ep.Config(w.T, w.H, w.k, w.E, w.R, fp8=w.fp8, num_workgroups=num_workgroups)
+
+
+class GpuRun:
+    """Device state of one workload: inputs, handle, receive buffers."""
+
+    def __init__(self, w, num_workgroups=0, capacity=None, fp8=None, poison=True):
+        self.w = w
+        self.cfg = config_of(w, num_workgroups)
+        if fp8 is not None:
+            self.cfg.fp8 = fp8
+        self.idx = to_dev(w.topk_idx)
+        self.x = to_dev(w.x)
+        self.wts = to_dev(w.topk_w)
+        self.h = Handle.alloc(self.cfg, DEV)
+        if poison:
+            for t in vars(self.h).values():
+                t.view(torch.uint8).fill_(POISON)
+        self.ws = alloc_workspace(self.cfg, DEV)
+        self.ws.fill_(POISON)
+        self.cap = ep.ep_recv_capacity_rows(self.cfg) if capacity is None else capacity
+        self.recv = None
+
+    # ---------------------------------------------------------- layout
+    def layout(self):
+        ep.ep_layout(self.cfg, self.idx, self.h, self.ws)
+        return self
+
+    def handle_np(self) -> dict:
+        torch.cuda.synchronize()
+        return {k: v.cpu().numpy() for k, v in vars(self.h).items()}
+
+    # --------------------------------------------------------- dispatch
+    def dispatch(self, fill=POISON):
+        if self.recv is None:
+            self.recv = RecvBuffers.alloc(self.cfg, self.cap, device=DEV, fill=fill)
+        ep.ep_dispatch(self.cfg, self.h, self.idx, self.x, self.recv.x, self.recv.scales, self.cap)
+        return self
+
+    def recv_np(self, rank_counts, full=False):
+        torch.cuda.synchronize()
+        xs, ss = [], []
+        for r in range(self.cfg.num_ranks):
+            n = self.cap if full else int(rank_counts[r])
+            xs.append(self.recv.x[r][:n].cpu().numpy())
+            if self.recv.scales is not None:
+                ss.append(self.recv.scales[r][:n].cpu().numpy())
+        if not self.cfg.fp8:
+            xs = [a.view(np.uint16) for a in xs]
+        return xs, (ss if self.recv.scales is not None else None)
+
+    # ---------------------------------------------------------- combine
+    def put_expert_rows(self, ys_np):
+        """Upload R arrays of valid rows into capacity-sized rank buffers."""
+        self.ybufs = []
+        for r, y in enumerate(ys_np):
+            b = torch.empty((self.cap, self.cfg.hidden), dtype=torch.int16, device=DEV)
+            b.view(torch.uint8).fill_(POISON)
+            if y.shape[0]:
+                b[:y.shape[0]] = to_dev(y)
+            self.ybufs.append(b)
+        return self
+
+    def combine(self, weights=True, out=None):
+        if out is None:
+            out = torch.empty((self.cfg.num_tokens, self.cfg.hidden), dtype=torch.int16, device=DEV)
+            out.view(torch.uint8).fill_(POISON)
+        ep.ep_combine(self.cfg, self.h, self.idx, self.ybufs, self.wts if weights else None, out,
+                      self.cap)
+        self.out = out
+        return self
+
+    def unpermute(self):
+        P = self.cfg.num_tokens * self.cfg.num_topk
+        u = torch.empty((P, self.cfg.hidden), dtype=torch.int16, device=DEV)
+        u.view(torch.uint8).fill_(POISON)
+        ep.ep_unpermute(self.cfg, self.h, self.idx, self.ybufs, u, self.cap)
+        return u
+
+
+def rel_err(g_bits: np.ndarray, r_bits: np.ndarray) -> float:
+    """max |g - r| / max(|r|, 1e-3) over bf16 outputs (the combine tolerance)."""
+    g = (g_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    r = (r_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return float(np.max(np.abs(g - r) / np.maximum(np.abs(r), 1e-3))) if g.size else 0.0

@@ -1,0 +1,135 @@
+"""CPU-side checks of the C ABI: libep.so loads, exports every function that
+include/ep.h declares, and its host-only calls (size helpers, status text,
+argument validation) behave as documented.  No kernel is launched here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import combine_ep_layout_03_amd as ep
+from combine_ep_layout_03_amd import _lib, build as epbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if epbuild.is_stale():
+        epbuild.build()
+    return ep.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][A-Za-z0-9_ \*]*?\b(ep_[a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (ep_[a-z_]+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (EP_[A-Z0-9_]+) (\d+)u?\b", text))
+    for name in ("EP_OK", "EP_ERR_INVALID_ARG", "EP_ERR_UNSUPPORTED", "EP_ERR_CAPACITY",
+                 "EP_ERR_HIP", "EP_DEVERR_INDEX", "EP_DEVERR_ROW", "EP_DEVERR_INTERNAL", "EP_DTYPE_BF16",
+                 "EP_DTYPE_FP8_E4M3", "EP_MAX_RANKS", "EP_MAX_TOPK", "EP_MAX_EXPERTS",
+                 "EP_MAX_HIDDEN"):
+        assert int(consts[name]) == getattr(_lib, name), name
+    assert int(consts["EP_ABI_VERSION"]) == ep.ep_abi_version()
+    # struct layouts: 7 int32 fields, 7 pointers
+    assert ctypes.sizeof(_lib.ep_config) == 28
+    assert ctypes.sizeof(_lib.ep_layout_t) == 56
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert ep.ep_status_string(s)
+    assert ep.ep_status_string(99) == "unknown status"
+
+
+def test_capacity_and_workspace(lib):
+    c = ep.Config(8192, 7168, 8, 256, 8, fp8=True)
+    assert ep.ep_recv_capacity_rows(c) == 8192 * 8
+    assert ep.ep_layout_workspace_bytes(c) == 64 * 257 * 4  # 64 chunks of 1024 pairs
+    c = ep.Config(128, 7168, 8, 288, 36, fp8=True)
+    assert ep.ep_layout_workspace_bytes(c) == 1 * 289 * 4
+    # many pairs, many experts: the chunk count is capped so the table stays small
+    c = ep.Config(1 << 20, 256, 8, 2048, 8)
+    ws = ep.ep_layout_workspace_bytes(c)
+    assert ws <= 65536 * 4 + 2049 * 4 * 4 and ws % (2049 * 4) == 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(num_tokens=0), dict(hidden=7), dict(hidden=100, fp8=True), dict(num_topk=0),
+    dict(num_topk=33), dict(num_experts=255), dict(num_ranks=65, num_experts=65 * 4),
+    dict(num_experts=4096, num_ranks=8), dict(num_workgroups=-1), dict(hidden=65544),
+])
+def test_invalid_configs_rejected(lib, bad):
+    base = dict(num_tokens=16, hidden=256, num_topk=2, num_experts=16, num_ranks=4, fp8=False)
+    base.update(bad)
+    c = ep.Config(**base)
+    assert ep.ep_recv_capacity_rows(c) == -1
+    assert ep.ep_layout_workspace_bytes(c) == 0
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_layout(c, 1, _lib.ep_layout_t(*([8] * 7)), 8, 0)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+
+
+def test_null_pointers_and_capacity_rejected_before_any_launch(lib):
+    c = ep.Config(16, 256, 2, 16, 4)
+    h = _lib.ep_layout_t(*([8] * 7))
+    hnull = _lib.ep_layout_t(*([8] * 6 + [None]))
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_layout(c, None, h, 8, 0)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_layout(c, 8, hnull, 8, 0)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_layout(c, 8, h, None, 0)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_dispatch(c, h, 8, 8, [8] * 4, None, 31, 0)
+    assert ei.value.status == ep.EP_ERR_CAPACITY
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_dispatch(c, h, 8, 8, [8, 8, None, 8], None, 32, 0)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    cf = ep.Config(16, 256, 2, 16, 4, fp8=True)
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_dispatch(cf, h, 8, 8, [8] * 4, None, 32, 0)   # FP8 needs scale buffers
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_combine(c, h, 8, [8] * 4, None, None, 32, 0)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_combine(c, h, 8, [8] * 4, None, 8, 10, 0)
+    assert ei.value.status == ep.EP_ERR_CAPACITY
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_unpermute(c, h, 8, [8, None, 8, 8], 8, 32, 0)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    missing = str(tmp_path / "libep.so")
+    saved = _lib._lib
+    _lib._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            _lib.load(missing)
+    finally:
+        _lib._lib = saved
