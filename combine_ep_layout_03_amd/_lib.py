@@ -55,7 +55,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError("libep.so is not built (%s); run __graft_entry__.build() or "
                            "python combine_ep_layout_03_amd/build.py" % path)
-    L = ctypes.CDLL(path)
+    _lib = configure(ctypes.CDLL(path))
+    return _lib
+
+
+def configure(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Declare the C signatures of include/ep.h on a loaded library."""
     vp, i64, cfgp, hp = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ep_config), ctypes.POINTER(ep_layout_t)
     L.ep_abi_version.restype = ctypes.c_uint32
     L.ep_abi_version.argtypes = []
@@ -73,7 +78,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.ep_combine.argtypes = [cfgp, hp, vp, ctypes.POINTER(vp), vp, vp, i64, vp]
     L.ep_unpermute.restype = ctypes.c_int32
     L.ep_unpermute.argtypes = [cfgp, hp, vp, ctypes.POINTER(vp), vp, i64, vp]
-    _lib = L
     return L
 
 

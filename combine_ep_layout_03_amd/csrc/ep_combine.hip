@@ -10,20 +10,26 @@
 // performa" (BF16 combine); [torchtitan PR] "Integrate DeepEP to experimental
 // torchtitan" (the token unpermute after the experts).
 //
-// Design: one wavefront per output token (grid-stride).  Lanes 0..k-1 resolve
-// the token's k received rows and weights; each lane then owns 8 channels
-// (16 B) per step, issues the k gathered 16-byte loads of a step before any
-// arithmetic (up to 8 rows in flight per lane), and folds them in ascending j
-// with fp32 fused multiply-adds from +0.  Each output element is written once
-// (16-byte stores, bf16 nearest-even); there are no atomics.  The un-permute
-// is fused into the loads; ep_unpermute exposes it on its own for tests.
+// Design.  The work unit is one (token, segment) pair, where a segment is
+// 128 16-byte chunks (1024 channels) of the output row; one single-wave
+// workgroup takes one unit at a time (grid-stride), so a token's row is spread
+// over several short-lived waves.  Lanes 0..k-1 resolve the token's k received
+// rows and weights; each lane then owns two chunks (c and c+64) and issues the
+// 2*k gathered 16-byte non-temporal loads of its chunks (up to 16 in flight)
+// before any arithmetic, folds them in ascending j with fp32 fused
+// multiply-adds from +0, rounds to bf16 nearest-even and writes each output
+// chunk once with a non-temporal store.  No atomics; the un-permute is fused
+// into the loads.  (Measured on MI355X at T=8192, H=7168, k=8: one-wave
+// workgroups and two chunks per lane beat four-wave workgroups, one chunk and
+// four chunks per lane; plain stores are slower than non-temporal ones.)
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
 
 constexpr int kThreads = kRowWaves * kWave;
-constexpr int kJB = 8;  // rows whose loads are issued together
+constexpr int kJB = 8;                 // rows whose loads are issued together
+constexpr int kSegChunks = 2 * kWave;  // 16-byte chunks per work unit
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline uint64_t readlane64(uint64_t v, int lane) {
@@ -37,6 +43,22 @@ __device__ inline uint32_t bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// acc[0..7] += w * (8 bf16 of v), element by element, one fma each.
+__device__ inline void fma8(float *acc, float w, u32x4 v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] = __builtin_fmaf(w, __uint_as_float(v[i] << 16), acc[2 * i]);
+    acc[2 * i + 1] = __builtin_fmaf(w, __uint_as_float(v[i] & 0xFFFF0000u), acc[2 * i + 1]);
+  }
+}
+
+__device__ inline u32x4 pack8(const float *acc) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = bf16_bits(acc[2 * i]) | (bf16_bits(acc[2 * i + 1]) << 16);
+  return o;
 }
 
 // Lane j < k: byte address of pair (t, j)'s received row (0 if unusable,
@@ -64,8 +86,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   if (*err != 0) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int nch = H / 8;
-  for (int64_t t = (int64_t)blockIdx.x * kRowWaves + wave; t < T;
-       t += (int64_t)gridDim.x * kRowWaves) {
+  const int nseg = (nch + kSegChunks - 1) / kSegChunks;
+  const int64_t units = (int64_t)T * nseg;
+  for (int64_t u = (int64_t)blockIdx.x * kRowWaves + wave; u < units;
+       u += (int64_t)gridDim.x * kRowWaves) {
+    const int64_t t = u / nseg;
+    const int c0 = (int)(u % nseg) * kSegChunks + lane;
+    const int c1 = c0 + kWave;
+    const bool ok0 = c0 < nch, ok1 = c1 < nch;
     uint64_t src = 0;
     float wj = 0.0f;
     if (lane < k) {
@@ -73,37 +101,31 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
       wj = w ? w[t * k + lane] : 1.0f;
     }
     if (__ballot(lane < k && src == 0) != 0) continue;  // a bad row: write nothing for t
-    u32x4 *orow = reinterpret_cast<u32x4 *>(out + t * H);
-    for (int c = lane; c < nch; c += kWave) {
-      float acc[8];
+    float acc0[8], acc1[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-      for (int j0 = 0; j0 < k; j0 += kJB) {
-        u32x4 v[kJB];
+    for (int i = 0; i < 8; ++i) acc0[i] = acc1[i] = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += kJB) {
+      u32x4 v0[kJB], v1[kJB];
 #pragma unroll
-        for (int jj = 0; jj < kJB; ++jj) {
-          if (j0 + jj < k) {
-            const u32x4 *yrow = reinterpret_cast<const u32x4 *>(readlane64(src, j0 + jj));
-            v[jj] = __builtin_nontemporal_load(yrow + c);
-          }
-        }
-#pragma unroll
-        for (int jj = 0; jj < kJB; ++jj) {
-          if (j0 + jj < k) {
-            const float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j0 + jj));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              acc[2 * i] = __builtin_fmaf(wv, __uint_as_float(v[jj][i] << 16), acc[2 * i]);
-              acc[2 * i + 1] = __builtin_fmaf(wv, __uint_as_float(v[jj][i] & 0xFFFF0000u), acc[2 * i + 1]);
-            }
-          }
+      for (int jj = 0; jj < kJB; ++jj) {
+        if (j0 + jj < k) {
+          const u32x4 *yrow = reinterpret_cast<const u32x4 *>(readlane64(src, j0 + jj));
+          if (ok0) v0[jj] = __builtin_nontemporal_load(yrow + c0);
+          if (ok1) v1[jj] = __builtin_nontemporal_load(yrow + c1);
         }
       }
-      u32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = bf16_bits(acc[2 * i]) | (bf16_bits(acc[2 * i + 1]) << 16);
-      __builtin_nontemporal_store(o, orow + c);
+      for (int jj = 0; jj < kJB; ++jj) {
+        if (j0 + jj < k) {
+          const float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j0 + jj));
+          fma8(acc0, wv, v0[jj]);
+          fma8(acc1, wv, v1[jj]);
+        }
+      }
     }
+    u32x4 *orow = reinterpret_cast<u32x4 *>(out + t * H);
+    if (ok0) __builtin_nontemporal_store(pack8(acc0), orow + c0);
+    if (ok1) __builtin_nontemporal_store(pack8(acc1), orow + c1);
   }
 }
 
@@ -131,7 +153,8 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(
 hipError_t launch_combine(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
                           const RankCPtrs &ry, const float *w, void *out, int64_t capacity_rows,
                           hipStream_t s) {
-  const int grid = row_grid(c, c.num_tokens);
+  const int64_t nseg = (c.hidden / 8 + kSegChunks - 1) / kSegChunks;
+  const int grid = row_grid(c, (int64_t)c.num_tokens * nseg);
   hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kThreads), 0, s, topk_idx, h.slot_of,
                      h.rank_offsets, h.error_flag, w, c.num_tokens, c.hidden, c.num_topk,
                      c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,

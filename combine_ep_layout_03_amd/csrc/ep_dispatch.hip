@@ -1,4 +1,4 @@
-// ep_dispatch.hip -- dispatch on gfx950: gather every token row into the
+// ep_dispatch.hip -- dispatch on gfx950: copy every token row into the
 // receive buffers of its k experts' ranks, optionally quantized to FP8.
 //
 // Pages: [DeepEP overview] "DeepSeek merilis library open source DeepEP ...",
@@ -8,25 +8,31 @@
 // DeepSeek deployment", "Magntölun" (activation scales over 128-element
 // vectors, computed on the fly; the horizontal amax is the awkward part).
 //
-// Design: one wavefront per token (grid-stride over tokens).  The token row
-// is read once; FP8 quantization is done once per token, and the k copies are
-// written with 16-byte non-temporal stores (rows are streamed out, never
-// re-read by this kernel).  Lanes 0..k-1 resolve the k destination rows; the
-// row base addresses are then taken with readlane, so every copy is a
-// scalar-base + vector-offset store.
-//   BF16: lane = 8 channels (16 B).
-//   FP8:  lane = 16 channels (2 x 16 B of bf16 -> 16 B of E4M3); 8 lanes form
-//         one 128-channel block, so a wave covers 8 blocks per step and the
-//         block amax is 3 xor-shuffles.  amax is taken on the bf16 bit
-//         patterns (|x| is monotone in its low 15 bits), the scale is the
+// Design.  The work unit is one (token, segment) pair and one single-wave
+// workgroup takes one unit at a time (grid-stride), so a token's row is spread
+// over several short-lived waves.  Each unit's slice of the token row is read
+// once and, for FP8, quantized once; lanes 0..k-1 resolve the k destination
+// rows and their base addresses are taken with readlane, so each of the k
+// copies is a scalar-base + vector-offset 16-byte non-temporal store.
+//   BF16: a segment is 64 chunks of 16 B (512 channels), one chunk per lane.
+//   FP8:  a segment is 8 blocks of 128 channels; a lane holds 16 channels
+//         (2 x 16 B of bf16 -> 16 B of E4M3), so 8 lanes form one block and
+//         the block amax takes 3 xor-shuffles.  amax is taken on the bf16 bit
+//         patterns (|x| is monotone in the low 15 bits), the scale is the
 //         correctly rounded binary32 a/448 and every code is E4M3 of the
-//         correctly rounded binary32 quotient x/s.
+//         correctly rounded binary32 quotient x/s; the lane that holds a
+//         block's first channels writes its scale into each copy.
+// (Measured on MI355X at T=8192, H=7168, k=8: one-wave units beat one wave per
+// token, four-wave workgroups, token-per-workgroup with LDS-staged scales,
+// copy-per-wave splits and plain stores; the scattered row stores, not the
+// quantization arithmetic, bound this kernel.)
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
 
 constexpr int kThreads = kRowWaves * kWave;
+constexpr int kFp8SegBlocks = 8;  // 128-channel blocks per FP8 work unit (= 64 lanes x 16 ch)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline uint64_t readlane64(uint64_t v, int lane) {
@@ -62,7 +68,7 @@ __device__ inline uint32_t bf16_absbits_max(u32x4 v, uint32_t m) {
   return m;
 }
 
-// 4 bf16 pairs -> 8 E4M3 codes (2 dwords), each code of (x / s).
+// 4 bf16 pairs -> 8 E4M3 codes of (x / s) in 2 dwords, channel order kept.
 __device__ inline void quant8(u32x4 v, float s, bool zero, uint32_t &w0, uint32_t &w1) {
   uint32_t c[8];
 #pragma unroll
@@ -106,8 +112,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
   if (*err != 0) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int nch = H / 8;  // 16-byte chunks per row
-  for (int64_t t = (int64_t)blockIdx.x * kRowWaves + wave; t < T;
-       t += (int64_t)gridDim.x * kRowWaves) {
+  const int nseg = (nch + kWave - 1) / kWave;
+  const int64_t units = (int64_t)T * nseg;
+  for (int64_t u = (int64_t)blockIdx.x * kRowWaves + wave; u < units;
+       u += (int64_t)gridDim.x * kRowWaves) {
+    const int64_t t = u / nseg;
+    const int c = (int)(u % nseg) * kWave + lane;
     uint64_t dst = 0;
     if (lane < k) {
       int32_t r;
@@ -116,13 +126,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
                      (const void *const *)rx.p, (int64_t)H * 2, r, row);
     }
     if (__ballot(lane < k && dst == 0) != 0) continue;  // a bad row: write nothing for t
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + t * H);
-    for (int c = lane; c < nch; c += kWave) {
-      const u32x4 v = __builtin_nontemporal_load(src + c);
-      for (int j = 0; j < k; ++j) {
-        u32x4 *d = reinterpret_cast<u32x4 *>(readlane64(dst, j));
-        __builtin_nontemporal_store(v, d + c);
-      }
+    const bool ok = c < nch;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (ok) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + t * H) + c);
+    for (int j = 0; j < k; ++j) {
+      u32x4 *d = reinterpret_cast<u32x4 *>(readlane64(dst, j));
+      if (ok) __builtin_nontemporal_store(v, d + c);
     }
   }
 }
@@ -135,8 +144,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
   if (*err != 0) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int nb = H / 128;  // 128-channel blocks per row
-  for (int64_t t = (int64_t)blockIdx.x * kRowWaves + wave; t < T;
-       t += (int64_t)gridDim.x * kRowWaves) {
+  const int nseg = (nb + kFp8SegBlocks - 1) / kFp8SegBlocks;
+  const int64_t units = (int64_t)T * nseg;
+  for (int64_t u = (int64_t)blockIdx.x * kRowWaves + wave; u < units;
+       u += (int64_t)gridDim.x * kRowWaves) {
+    const int64_t t = u / nseg;
+    const int blk = (int)(u % nseg) * kFp8SegBlocks + lane / 8;
     uint64_t qdst = 0, sdst = 0;
     if (lane < k) {
       int32_t r = 0;
@@ -145,34 +158,32 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
                       (const void *const *)rq.p, (int64_t)H, r, row);
       if (qdst) sdst = (uint64_t)(rs.p[r] + row * nb);
     }
-    if (__ballot(lane < k && qdst == 0) != 0) continue;
+    if (__ballot(lane < k && qdst == 0) != 0) continue;  // a bad row: write nothing for t
+    const bool valid = blk < nb;
+    const int ch = blk * 128 + (lane % 8) * 16;
     const uint16_t *xrow = x + t * H;
-    for (int b0 = 0; b0 < nb; b0 += 8) {
-      const int blk = b0 + lane / 8;
-      const bool valid = blk < nb;
-      const int ch = blk * 128 + (lane % 8) * 16;
-      u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+    u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+    if (valid) {
+      v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch));
+      v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch + 8));
+    }
+    // 8 lanes per block: invalid lanes form whole groups of 8 and stay at 0
+    uint32_t m = bf16_absbits_max(v1, bf16_absbits_max(v0, 0u));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 4, kWave));
+    const bool zero = (m == 0u);
+    const float s = zero ? 0.0f : __uint_as_float(m << 16) / 448.0f;
+    uint32_t q0, q1, q2, q3;
+    quant8(v0, s, zero, q0, q1);
+    quant8(v1, s, zero, q2, q3);
+    const u32x4 q = {q0, q1, q2, q3};
+    for (int j = 0; j < k; ++j) {
+      uint8_t *d = reinterpret_cast<uint8_t *>(readlane64(qdst, j));
+      float *sd = reinterpret_cast<float *>(readlane64(sdst, j));
       if (valid) {
-        v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch));
-        v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch + 8));
-      }
-      uint32_t m = bf16_absbits_max(v1, bf16_absbits_max(v0, 0u));
-      m = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
-      m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
-      m = max(m, (uint32_t)__shfl_xor((int)m, 4, kWave));
-      const bool zero = (m == 0u);
-      const float s = zero ? 0.0f : __uint_as_float(m << 16) / 448.0f;
-      uint32_t q0, q1, q2, q3;
-      quant8(v0, s, zero, q0, q1);
-      quant8(v1, s, zero, q2, q3);
-      const u32x4 q = {q0, q1, q2, q3};
-      for (int j = 0; j < k; ++j) {
-        uint8_t *d = reinterpret_cast<uint8_t *>(readlane64(qdst, j));
-        float *sd = reinterpret_cast<float *>(readlane64(sdst, j));
-        if (valid) {
-          __builtin_nontemporal_store(q, reinterpret_cast<u32x4 *>(d + ch));
-          if ((lane % 8) == 0) sd[blk] = s;
-        }
+        __builtin_nontemporal_store(q, reinterpret_cast<u32x4 *>(d + ch));
+        if ((lane % 8) == 0) sd[blk] = s;
       }
     }
   }
@@ -183,14 +194,17 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
 hipError_t launch_dispatch(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
                            const void *x, const RankPtrs &rx, const ScalePtrs &rs,
                            int64_t capacity_rows, hipStream_t s) {
-  const int grid = row_grid(c, c.num_tokens);
   const int32_t El = c.num_experts / c.num_ranks;
   if (c.dispatch_dtype == EP_DTYPE_FP8_E4M3) {
+    const int64_t nseg = (c.hidden / 128 + kFp8SegBlocks - 1) / kFp8SegBlocks;
+    const int grid = row_grid(c, (int64_t)c.num_tokens * nseg);
     hipLaunchKernelGGL(dispatch_fp8_kernel, dim3(grid), dim3(kThreads), 0, s,
                        static_cast<const uint16_t *>(x), topk_idx, h.slot_of, h.rank_offsets,
                        h.error_flag, c.num_tokens, c.hidden, c.num_topk, c.num_experts, El,
                        capacity_rows, rx, rs);
   } else {
+    const int64_t nseg = (c.hidden / 8 + kWave - 1) / kWave;
+    const int grid = row_grid(c, (int64_t)c.num_tokens * nseg);
     hipLaunchKernelGGL(dispatch_bf16_kernel, dim3(grid), dim3(kThreads), 0, s,
                        static_cast<const uint16_t *>(x), topk_idx, h.slot_of, h.rank_offsets,
                        h.error_flag, c.num_tokens, c.hidden, c.num_topk, c.num_experts, El,

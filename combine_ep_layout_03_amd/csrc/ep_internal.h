@@ -24,16 +24,22 @@ struct ScalePtrs {
 // Layout plan: the P = T*k pairs are cut into C chunks of S pairs; one
 // wavefront owns one chunk in both layout kernels.
 struct LayoutPlan {
+  bool small;  // single-workgroup path
   int64_t P;
   int32_t S;  // pairs per chunk (multiple of 64)
   int32_t C;  // chunks
   int32_t workgroups;  // ceil(C / kLayoutWaves)
-  size_t workspace_bytes;  // C * (E + 1) * 4: per-chunk histograms + bad-index column
+  size_t workspace_bytes;  // (E + 1) * C * 4: chunk histograms, expert-major, + bad-index row
 };
 
 constexpr int kWave = 64;
 constexpr int kLayoutWaves = 4;  // wavefronts per layout workgroup
-constexpr int kRowWaves = 4;     // wavefronts per dispatch / combine workgroup
+constexpr int kLayoutMaxChunks = kLayoutWaves * kWave;  // C <= threads of a layout workgroup
+constexpr int kLayoutChunk = 512;  // pairs per chunk (= per wavefront) of the two-launch layout
+constexpr int kRowWaves = 1;     // wavefronts per dispatch / combine workgroup
+constexpr int kSmallWaves = 16;  // wavefronts of the single-workgroup layout
+constexpr int64_t kSmallMaxPairs = 8192;    // T*k limit of the single-launch layout
+constexpr int kSmallMaxExperts = 384;       // E limit of the single-launch layout (LDS <= 64 KB)
 
 LayoutPlan plan_layout(int64_t P, int E);
 
@@ -53,10 +59,12 @@ hipError_t launch_combine(const ep_config &c, const ep_layout_t &h, const int32_
 hipError_t launch_unpermute(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
                             const RankCPtrs &ry, void *out, int64_t capacity_rows, hipStream_t s);
 
-// Grid size for the per-token kernels: num_workgroups or ceil(T / waves).
+// Grid size of the per-row kernels: num_workgroups, else one single-wave
+// workgroup per work unit (the kernels grid-stride over the rest, if any).
 inline int row_grid(const ep_config &c, int64_t units) {
   if (c.num_workgroups > 0) return c.num_workgroups;
   int64_t g = (units + kRowWaves - 1) / kRowWaves;
+  if (g > 0x7FFFFFFF) g = 0x7FFFFFFF;
   return (int)(g < 1 ? 1 : g);
 }
 

@@ -8,21 +8,26 @@
 // (a GEMM layout: experts contiguous) and "Pola penggunaan ..." (the handle
 // carries per-expert token counts for the GEMM).
 //
-// Design (two launches, no global atomics, bit-identical on every run):
-//   count   -- the T*k pairs are cut into C chunks of S pairs; one wavefront
-//              builds its chunk's expert histogram in LDS and stores it as
-//              row c of a [C][E+1] table (column E counts bad indices).
-//   scatter -- every workgroup reads the whole table (C*(E+1) ints, L2
-//              resident), so each has the expert totals, their exclusive
-//              scan and, for its own chunks, the counts of all earlier chunks;
-//              workgroup 0 writes the handle's counts / offsets / error word.
-//              Each wavefront then walks its chunk 64 pairs at a time in
+// Design (deterministic: no order-dependent atomics, identical bytes on every
+// run).  The T*k pairs are cut into chunks, one chunk per wavefront:
+//   count   -- each wavefront builds its chunk's expert histogram in LDS;
+//   scan    -- expert totals, their exclusive scan (expert_offsets), rank
+//              ranges, and for every chunk the counts of all earlier chunks;
+//   walk    -- each wavefront walks its chunk 64 pairs at a time in
 //              ascending order: lanes naming the same expert are found with
 //              ceil(log2 E) ballots, a lane's rank among them is
 //              popcount(match & lanes-below), and the group's highest lane
 //              advances the expert's running base in LDS.  This reproduces
-//              "slot = offset[e] + #earlier pairs of e" without any
-//              order-dependent atomic.
+//              "slot = offset[e] + #earlier pairs of e" exactly.
+// Small problems (P <= kSmallMaxPairs, E <= kSmallMaxExperts, e.g. decode
+// batches) run all three phases in ONE launch of one 16-wave workgroup (its
+// waves are the chunks).  Larger ones use two launches: a count kernel writes
+// an expert-major [E+1][C] table of chunk histograms (row E counts bad
+// indices) to the workspace, and a scatter kernel in which every workgroup
+// reads that L2-resident table (16-byte loads, all in flight) to get the
+// totals and its own chunks' prefixes before walking.  (Measured at T*k =
+// 65536: making every workgroup of one launch count all pairs itself costs
+// more in LDS atomics than the second launch does.)
 #include "ep_internal.h"
 
 namespace ep {
@@ -30,11 +35,25 @@ namespace ep {
 LayoutPlan plan_layout(int64_t P, int E) {
   LayoutPlan p{};
   p.P = P;
+  if (P <= kSmallMaxPairs && E <= kSmallMaxExperts) {
+    // single launch: G workgroups of kSmallWaves waves, ~4096 pairs each
+    int64_t G = (P + 4095) / 4096;
+    if (G < 1) G = 1;
+    if (G > 64) G = 64;
+    const int64_t unit = (int64_t)kSmallWaves * kWave;
+    const int64_t S = ((P + G - 1) / G + unit - 1) / unit * unit;
+    p.small = true;
+    p.S = (int32_t)S;
+    p.C = (int32_t)((P + S - 1) / S);
+    p.workgroups = p.C;
+    p.workspace_bytes = 256;  // unused; a minimal buffer keeps the contract uniform
+    return p;
+  }
   // Bound the table every scatter workgroup reads to ~64K entries.
   int64_t cmax = 65536 / (E + 1);
   if (cmax < 4) cmax = 4;
-  if (cmax > 256) cmax = 256;
-  int64_t S = 1024;
+  if (cmax > kLayoutMaxChunks) cmax = kLayoutMaxChunks;
+  int64_t S = kLayoutChunk;
   int64_t C = (P + S - 1) / S;
   if (C > cmax) {
     S = ((P + cmax - 1) / cmax + kWave - 1) / kWave * kWave;
@@ -52,6 +71,11 @@ namespace {
 
 constexpr int kThreads = kLayoutWaves * kWave;
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Chunk histograms: wave c counts the pairs [c*S, c*S+S) in LDS and writes
+// column c of the expert-major table hist[E+1][C] (row E counts indices
+// outside [0,E)).
 __global__ __launch_bounds__(kThreads) void layout_count_kernel(const int32_t *__restrict__ idx,
                                                                  int64_t P, int32_t E, int32_t S,
                                                                  int32_t C,
@@ -66,14 +90,33 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(const int32_t *_
   if (c < C) {
     const int64_t p0 = c * S;
     const int64_t p1 = (p0 + S < P) ? p0 + S : P;
-    for (int64_t p = p0 + lane; p < p1; p += kWave) {
-      const int32_t e = idx[p];
-      atomicAdd(&h[((uint32_t)e < (uint32_t)E) ? e : E], 1);
+    const bool vec = (((uintptr_t)(idx + p0)) & 15u) == 0;
+    // 16 pairs per lane per batch (4 x 16-byte loads in flight)
+    for (int64_t q = p0; q < p1; q += 16 * kWave) {
+      i32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t p = q + ((int64_t)u * kWave + lane) * 4;
+        if (vec && p + 4 <= p1) {
+          v[u] = *reinterpret_cast<const i32x4 *>(idx + p);
+        } else {
+          i32x4 t = {0, 0, 0, 0};
+          for (int i = 0; i < 4; ++i) t[i] = (p + i < p1) ? idx[p + i] : 0;
+          v[u] = t;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t p = q + ((int64_t)u * kWave + lane) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (p + i < p1) atomicAdd(&h[((uint32_t)v[u][i] < (uint32_t)E) ? v[u][i] : E], 1);
+      }
     }
   }
   __syncthreads();
   if (c < C)
-    for (int e = lane; e < E1; e += kWave) hist[c * E1 + e] = h[e];
+    for (int e = lane; e < E1; e += kWave) hist[(int64_t)e * C + c] = h[e];
 }
 
 __device__ inline int32_t wave_inclusive_scan(int32_t v, int lane) {
@@ -85,11 +128,12 @@ __device__ inline int32_t wave_inclusive_scan(int32_t v, int lane) {
   return v;
 }
 
-// Exclusive scan of a[0..n) in place, a[n] = total.  All kThreads threads
-// call it; `wsum` holds kLayoutWaves ints of LDS.
+// Exclusive scan of a[0..n) in place, a[n] = total.  All NT threads of the
+// workgroup call it; `wsum` holds NT/64 ints of LDS.
+template <int NT>
 __device__ void block_exclusive_scan(int32_t *a, int n, int32_t *wsum) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int per = (n + kThreads - 1) / kThreads;
+  const int per = (n + NT - 1) / NT;
   const int b = (tid * per < n) ? tid * per : n;
   const int end = (b + per < n) ? b + per : n;
   int32_t s = 0;
@@ -105,8 +149,173 @@ __device__ void block_exclusive_scan(int32_t *a, int n, int32_t *wsum) {
     a[i] = run;
     run += v;
   }
-  if (tid == kThreads - 1) a[n] = pre + incl;
+  if (tid == NT - 1) a[n] = pre + incl;
   __syncthreads();
+}
+
+// Counts, offsets, rank ranges and error word from the scanned offsets
+// off[0..E] (every thread of the workgroup takes part).
+template <int NT>
+__device__ void write_handle(const int32_t *off, int32_t E, int32_t R, int32_t nbad,
+                             const ep_layout_t &h) {
+  const int tid = threadIdx.x;
+  const int32_t El = E / R;
+  for (int e = tid; e < E; e += NT) {
+    h.expert_counts[e] = off[e + 1] - off[e];
+    h.expert_offsets[e] = off[e];
+  }
+  for (int r = tid; r < R; r += NT) {
+    h.rank_offsets[r] = off[r * El];
+    h.rank_counts[r] = off[(r + 1) * El] - off[r * El];
+  }
+  if (tid == 0) {
+    h.expert_offsets[E] = off[E];
+    h.rank_offsets[R] = off[E];
+    h.error_flag[0] = nbad ? (int32_t)EP_DEVERR_INDEX : 0;
+  }
+}
+
+constexpr int kStage = 16 * kWave;       // pairs a scatter-kernel wave stages in LDS at a time
+constexpr int kSmallStage = 8 * kWave;   // pairs a small-kernel wave stages (P <= 8192 -> <= 512)
+
+// One wavefront assigns the slots of pairs [p0, p1) in ascending order; bw[e]
+// holds the next free slot of expert e for this chunk and is advanced.  The
+// wave first copies 64*PL indices into its LDS stage (PL per lane, 16-byte
+// loads, one round trip), then ranks them 64 at a time in a rolled loop: the
+// layout runs few waves, each executing its code once, so compact loops
+// (warm instruction cache) beat unrolled straight-line code here.
+template <int PL>
+__device__ void wave_walk(const int32_t *__restrict__ idx, int64_t p0, int64_t p1, int64_t P,
+                          int32_t E, int32_t *bw, int32_t *stage, const ep_layout_t &h) {
+  static_assert(PL % 4 == 0, "whole 16-byte groups per lane");
+  constexpr int kSt = PL * kWave;
+  const int lane = threadIdx.x % kWave;
+  const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int64_t qb = p0; qb < p1; qb += kSt) {
+    const int64_t n = (p1 - qb < kSt) ? p1 - qb : kSt;
+    const int64_t pl = qb + (int64_t)lane * PL;
+    i32x4 v[PL / 4];
+    const bool vec = ((((uintptr_t)(idx + qb)) & 15u) == 0) && pl + PL <= qb + n;
+#pragma unroll
+    for (int u = 0; u < PL / 4; ++u) {
+      if (vec) {
+        v[u] = *reinterpret_cast<const i32x4 *>(idx + pl + 4 * u);
+      } else {
+        i32x4 t = {0, 0, 0, 0};
+        for (int i = 0; i < 4; ++i) t[i] = (pl + 4 * u + i < qb + n) ? idx[pl + 4 * u + i] : 0;
+        v[u] = t;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PL / 4; ++u) *reinterpret_cast<i32x4 *>(stage + lane * PL + 4 * u) = v[u];
+#pragma unroll 1
+    for (int i = 0; i * kWave < n; ++i) {
+      const int64_t p = qb + i * kWave + lane;
+      const bool valid = i * kWave + lane < n;
+      const int32_t e = valid ? stage[i * kWave + lane] : 0;
+      // lanes whose expert matches this lane's in every bit: m &= (bit ? B : ~B)
+      uint64_t m = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const uint32_t bit = ((uint32_t)e >> b) & 1u;
+        const uint64_t bb = __ballot(bit != 0u);
+        const uint32_t flip = bit - 1u;  // 0 if the bit is set, all ones if not
+        m &= bb ^ (((uint64_t)flip << 32) | flip);
+      }
+      if (valid) {
+        const int32_t slot = bw[e] + __popcll(m & below);
+        h.slot_of[p] = slot;
+        if ((uint64_t)(uint32_t)slot < (uint64_t)P) h.src_of[slot] = (int32_t)p;
+        else atomicOr(h.error_flag, (int32_t)EP_DEVERR_INTERNAL);  // cannot happen; never write out of range
+        if ((m >> lane) == 1ull) bw[e] += __popcll(m);  // the group's highest lane
+      }
+    }
+  }
+}
+
+constexpr int kSmallThreads = kSmallWaves * kWave;
+constexpr int kSmallRounds = 2;  // int4 loads per thread per batch (2 x 4096 pairs: P <= 8192 is one batch)
+
+// Single-launch layout: workgroup g owns pairs [g*S, g*S+S) (S a multiple of
+// kSmallWaves*64) and, inside it, wave w owns S/kSmallWaves pairs.  Every
+// workgroup streams ALL P indices (int4 loads, a batch of 16 per thread in
+// flight) and counts in LDS the expert totals, the pairs before its own
+// chunk, and its own waves' pairs, so no workgroup needs another's results.
+__global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
+    const int32_t *__restrict__ idx, int64_t P, int32_t E, int32_t R, int32_t S, ep_layout_t h) {
+  extern __shared__ int32_t lds[];
+  int32_t *tot = lds;                      // [E+1] totals, then exclusive offsets
+  int32_t *pre = tot + E + 1;              // [E]   pairs of e before this chunk
+  int32_t *cnt = pre + E;                  // [kSmallWaves][E]: own counts, then bases
+  int32_t *misc = cnt + kSmallWaves * E;   // [kSmallWaves] scan scratch, [kSmallWaves] bad
+  int32_t *stage = lds + (((kSmallWaves + 2) * E + 1 + 2 * kSmallWaves + 3) / 4 * 4);  // [kSmallWaves][kSmallStage]
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  for (int i = tid; i < (kSmallWaves + 2) * E + 1; i += kSmallThreads) lds[i] = 0;
+  __syncthreads();
+
+  const int64_t c0 = (int64_t)blockIdx.x * S;
+  const int64_t c1 = (c0 + S < P) ? c0 + S : P;
+  const int32_t Sw = S / kSmallWaves;
+  int32_t bad = 0;
+  // pairs covered by whole 16-byte loads (none if the caller's array is not 16-byte aligned)
+  const int64_t P4 = ((uintptr_t)idx & 15u) ? 0 : (P & ~(int64_t)3);
+  for (int64_t base = 0; base < P; base += (int64_t)kSmallRounds * kSmallThreads * 4) {
+    i32x4 v[kSmallRounds];
+#pragma unroll
+    for (int u = 0; u < kSmallRounds; ++u) {
+      const int64_t p = base + ((int64_t)u * kSmallThreads + tid) * 4;
+      if (p + 4 <= P4) {
+        v[u] = *reinterpret_cast<const i32x4 *>(idx + p);
+      } else {
+        i32x4 t = {-1, -1, -1, -1};
+        for (int i = 0; i < 4; ++i)
+          if (p + i < P) t[i] = idx[p + i];
+        v[u] = t;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSmallRounds; ++u) {
+      const int64_t p = base + ((int64_t)u * kSmallThreads + tid) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t q = p + i;
+        if (q < P) {
+          const int32_t e = v[u][i];
+          if ((uint32_t)e >= (uint32_t)E) {
+            ++bad;
+          } else {
+            atomicAdd(&tot[e], 1);
+            if (q < c0) atomicAdd(&pre[e], 1);
+            else if (q < c1) atomicAdd(&cnt[(int)((q - c0) / Sw) * E + e], 1);
+          }
+        }
+      }
+    }
+  }
+  bad = wave_inclusive_scan(bad, lane);
+  if (lane == kWave - 1) misc[kSmallWaves + wave] = bad;
+  __syncthreads();
+
+  // cnt[w][e] becomes pre[e] + the counts of this chunk's earlier waves
+  for (int e = tid; e < E; e += kSmallThreads) {
+    int32_t run = pre[e];
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) {
+      const int32_t c = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += c;
+    }
+  }
+  int32_t nbad = 0;
+  for (int w = 0; w < kSmallWaves; ++w) nbad += misc[kSmallWaves + w];
+  block_exclusive_scan<kSmallThreads>(tot, E, misc);  // synchronizes
+  if (blockIdx.x == 0) write_handle<kSmallThreads>(tot, E, R, nbad, h);
+  if (nbad) return;  // uniform: the handle's slots are unspecified on error
+  for (int i = tid; i < kSmallWaves * E; i += kSmallThreads) cnt[i] += tot[i % E];
+  __syncthreads();
+  const int64_t p0 = c0 + (int64_t)wave * Sw;
+  const int64_t p1 = (p0 + Sw < c1) ? p0 + Sw : c1;
+  wave_walk<kSmallStage / kWave>(idx, p0, p1, P, E, cnt + wave * E, stage + wave * kSmallStage, h);
 }
 
 __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
@@ -115,54 +324,67 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
   extern __shared__ int32_t lds[];
   int32_t *off = lds;                        // [E+1]
   int32_t *base = lds + (E + 1);             // [kLayoutWaves][E]
-  int32_t *misc = base + kLayoutWaves * E;   // [kLayoutWaves] scan scratch, [4] bad count
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  int32_t *misc = base + kLayoutWaves * E;   // [kLayoutWaves] scan scratch, [kLayoutWaves] bad counts
+  int32_t *stage = lds + ((E + 1) + kLayoutWaves * E + 8 + 3) / 4 * 4;  // [kLayoutWaves][kStage], 16-byte aligned
+  const int tid = threadIdx.x, wave = tid / kWave;
   const int E1 = E + 1;
-  const int32_t El = E / R;
   const int64_t c0 = (int64_t)blockIdx.x * kLayoutWaves;
 
-  // Totals over all chunks and, for this workgroup's chunks, the sums over
-  // the chunks before each of them.
-  for (int e = tid; e < E1; e += kThreads) {
-    int32_t run = 0;
-    const int64_t cpre = (c0 < C) ? c0 : C;
-#pragma unroll 8
-    for (int64_t c = 0; c < cpre; ++c) run += hist[c * E1 + e];
+  // Row e of the table holds expert e's count in every chunk: sum it for the
+  // total and, for this workgroup's chunks, the sums over the chunks before
+  // each of them (16-byte loads, 32 in flight per thread: one round trip for
+  // up to 128 chunks).
+  // c0 is a multiple of 4, so this workgroup's 4 chunks are one int4 group
+  const bool vec = (C % 4) == 0 && (((uintptr_t)hist) & 15u) == 0;
+  // Row E (indices outside [0,E)) is summed by all threads together, so no
+  // thread reads two rows when E is a multiple of the workgroup size.
+  // (the plan keeps C <= kThreads, so one element per thread; it is consumed
+  // only after the row loads below, so it adds no round trip)
+  int32_t badpart = (tid < C) ? hist[(int64_t)E * C + tid] : 0;
+  for (int e = tid; e < E; e += kThreads) {
+    const int32_t *row = hist + (int64_t)e * C;
+    int32_t run = 0, before = 0;
+    i32x4 mine = {0, 0, 0, 0};
+#pragma unroll 1
+    for (int cb = 0; cb < C; cb += 128) {
+      i32x4 v[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int c = cb + 4 * u;
+        if (vec && c + 4 <= C) {
+          v[u] = *reinterpret_cast<const i32x4 *>(row + c);
+        } else {
+          i32x4 t = {0, 0, 0, 0};
+          for (int i = 0; i < 4; ++i) t[i] = (c + i < C) ? row[c + i] : 0;
+          v[u] = t;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int c = cb + 4 * u;
+        const int32_t s4 = v[u][0] + v[u][1] + v[u][2] + v[u][3];
+        run += s4;
+        before += (c < c0) ? s4 : 0;
+        if (c == c0) mine = v[u];
+      }
+    }
     int32_t pre[kLayoutWaves];
+    pre[0] = before;
+    pre[1] = before + mine[0];
+    pre[2] = pre[1] + mine[1];
+    pre[3] = pre[2] + mine[2];
+    off[e] = run;
 #pragma unroll
-    for (int w = 0; w < kLayoutWaves; ++w) {
-      pre[w] = run;
-      if (c0 + w < C) run += hist[(c0 + w) * E1 + e];
-    }
-#pragma unroll 8
-    for (int64_t c = c0 + kLayoutWaves; c < C; ++c) run += hist[c * E1 + e];
-    if (e < E) {
-      off[e] = run;
-#pragma unroll
-      for (int w = 0; w < kLayoutWaves; ++w) base[w * E + e] = pre[w];
-    } else {
-      misc[kLayoutWaves] = run;
-    }
+    for (int w = 0; w < kLayoutWaves; ++w) base[w * E + e] = pre[w];
   }
+  badpart = wave_inclusive_scan(badpart, tid % kWave);
+  if (tid % kWave == kWave - 1) misc[kLayoutWaves + tid / kWave] = badpart;
   __syncthreads();
-  const int32_t nbad = misc[kLayoutWaves];
-  block_exclusive_scan(off, E, misc);
-
-  if (blockIdx.x == 0) {
-    for (int e = tid; e < E; e += kThreads) {
-      h.expert_counts[e] = off[e + 1] - off[e];
-      h.expert_offsets[e] = off[e];
-    }
-    for (int r = tid; r < R; r += kThreads) {
-      h.rank_offsets[r] = off[r * El];
-      h.rank_counts[r] = off[(r + 1) * El] - off[r * El];
-    }
-    if (tid == 0) {
-      h.expert_offsets[E] = off[E];
-      h.rank_offsets[R] = off[E];
-      h.error_flag[0] = nbad ? (int32_t)EP_DEVERR_INDEX : 0;
-    }
-  }
+  int32_t nbad = 0;
+#pragma unroll
+  for (int w = 0; w < kLayoutWaves; ++w) nbad += misc[kLayoutWaves + w];
+  block_exclusive_scan<kThreads>(off, E, misc);
+  if (blockIdx.x == 0) write_handle<kThreads>(off, E, R, nbad, h);
   if (nbad) return;  // uniform: the handle's slots are unspecified on error
 
   for (int i = tid; i < kLayoutWaves * E; i += kThreads) base[i] += off[i % E];
@@ -170,29 +392,9 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
 
   const int64_t c = c0 + wave;
   if (c >= C) return;
-  int32_t *bw = base + wave * E;
-  const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   const int64_t p0 = c * S;
   const int64_t p1 = (p0 + S < P) ? p0 + S : P;
-  for (int64_t q = p0; q < p1; q += kWave) {
-    const int64_t p = q + lane;
-    const bool valid = p < p1;
-    const int32_t e = valid ? idx[p] : 0;
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
-    }
-    if (valid) {
-      const int32_t slot = bw[e] + __popcll(m & below);
-      h.slot_of[p] = slot;
-      if ((uint64_t)(uint32_t)slot < (uint64_t)P) h.src_of[slot] = (int32_t)p;
-      else atomicOr(h.error_flag, (int32_t)EP_DEVERR_INTERNAL);  // cannot happen; never write out of range
-      if ((m >> lane) == 1ull) bw[e] += __popcll(m);  // the group's highest lane
-    }
-  }
+  wave_walk<kStage / kWave>(idx, p0, p1, P, E, base + wave * E, stage + wave * kStage, h);
 }
 
 }  // namespace
@@ -200,13 +402,22 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
 hipError_t launch_layout(const ep_config &c, const LayoutPlan &plan, const int32_t *topk_idx,
                          const ep_layout_t &h, void *workspace, hipStream_t s) {
   const int E = c.num_experts;
+  if (plan.small) {
+    const size_t lds = (((size_t)(kSmallWaves + 2) * E + 1 + 2 * kSmallWaves + 3) / 4 * 4 +
+                        (size_t)kSmallWaves * kSmallStage) * sizeof(int32_t);
+    hipLaunchKernelGGL(layout_small_kernel, dim3(plan.workgroups), dim3(kSmallThreads), lds, s,
+                       topk_idx, plan.P, E, c.num_ranks, plan.S, h);
+    return hipGetLastError();
+  }
   int32_t *hist = static_cast<int32_t *>(workspace);
   const size_t lds_count = (size_t)kLayoutWaves * (E + 1) * sizeof(int32_t);
   hipLaunchKernelGGL(layout_count_kernel, dim3(plan.workgroups), dim3(kThreads), lds_count, s,
                      topk_idx, plan.P, E, plan.S, plan.C, hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t lds_scatter = ((size_t)(E + 1) + (size_t)kLayoutWaves * E + 8) * sizeof(int32_t);
+  const size_t lds_scatter =
+      (((size_t)(E + 1) + (size_t)kLayoutWaves * E + 8 + 3) / 4 * 4 + (size_t)kLayoutWaves * kStage) *
+      sizeof(int32_t);
   hipLaunchKernelGGL(layout_scatter_kernel, dim3(plan.workgroups), dim3(kThreads), lds_scatter, s,
                      topk_idx, plan.P, E, c.num_ranks, plan.S, plan.C, (const int32_t *)hist, h);
   return hipGetLastError();

@@ -65,9 +65,12 @@ def test_status_strings(lib):
 def test_capacity_and_workspace(lib):
     c = ep.Config(8192, 7168, 8, 256, 8, fp8=True)
     assert ep.ep_recv_capacity_rows(c) == 8192 * 8
-    assert ep.ep_layout_workspace_bytes(c) == 64 * 257 * 4  # 64 chunks of 1024 pairs
+    assert ep.ep_layout_workspace_bytes(c) == 128 * 257 * 4  # 128 chunks of 512 pairs
+    # up to 8192 pairs and 512 experts the layout is one launch: no table
     c = ep.Config(128, 7168, 8, 288, 36, fp8=True)
-    assert ep.ep_layout_workspace_bytes(c) == 1 * 289 * 4
+    assert ep.ep_layout_workspace_bytes(c) == 256
+    c = ep.Config(30000, 7168, 8, 256, 8)  # 240000 pairs: chunks grow to 960 pairs so C <= 255
+    assert ep.ep_layout_workspace_bytes(c) == 250 * 257 * 4
     # many pairs, many experts: the chunk count is capped so the table stays small
     c = ep.Config(1 << 20, 256, 8, 2048, 8)
     ws = ep.ep_layout_workspace_bytes(c)

@@ -84,6 +84,15 @@ def layout_edge_cases():
     cases.append(("max_topk", 97, 32, 64, 8, rng.integers(0, 64, (97, 32))))
     cases.append(("max_experts", 2000, 8, 2048, 64, rng.integers(0, 2048, (2000, 8))))
     cases.append(("many_chunks_capped", 40000, 8, 2048, 8, rng.integers(0, 2048, (40000, 8))))
+    # the single-workgroup path at its limits, and the two-launch path just past them
+    cases.append(("small_path_max", 1024, 8, 384, 8, rng.integers(0, 384, (1024, 8))))
+    cases.append(("small_path_ragged", 1021, 8, 384, 16, rng.integers(0, 384, (1021, 8))))
+    cases.append(("small_E_over_limit", 1000, 8, 512, 16, rng.integers(0, 512, (1000, 8))))
+    cases.append(("two_launch_min", 1025, 8, 64, 8, rng.integers(0, 64, (1025, 8))))
+    cases.append(("two_launch_E256", 30000, 8, 256, 8, rng.integers(0, 256, (30000, 8))))
+    cases.append(("two_launch_ragged", 16385, 8, 512, 16, rng.integers(0, 512, (16385, 8))))
+    p1 = 1.0 / (1.0 + np.arange(256)) ** 1.1
+    cases.append(("two_launch_zipf", 20001, 8, 256, 8, rng.choice(256, (20001, 8), p=p1 / p1.sum())))
     p = 1.0 / (1.0 + np.arange(288)) ** 2
     cases.append(("zipf2", 5000, 8, 288, 36, rng.choice(288, (5000, 8), p=p / p.sum())))
     return cases
@@ -97,8 +106,25 @@ def test_layout_edge_cases(case):
     check_layout(w, GpuRun(w).layout())
 
 
-def test_layout_bad_index_sets_flag_and_blocks_writes():
-    T, H, k, E, R = 300, 256, 2, 16, 4
+@pytest.mark.parametrize("T", [1000, 20000])
+def test_layout_unaligned_index_array(T):
+    """topk_idx at a 4-byte (not 16-byte) aligned address."""
+    k, E, R = 3, 64, 8
+    rng = np.random.default_rng(T)
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    say(f"layout unaligned T={T}")
+    w = custom("unaligned", T, 8, k, E, R, False, idx)
+    run = GpuRun(w)
+    buf = torch.zeros(T * k + 1, dtype=torch.int32, device="cuda")
+    buf[1:] = torch.from_numpy(idx.ravel()).cuda()
+    run.idx = buf[1:]
+    assert run.idx.data_ptr() % 16 == 4
+    check_layout(w, run.layout())
+
+
+@pytest.mark.parametrize("T", [300, 70000])
+def test_layout_bad_index_sets_flag_and_blocks_writes(T):
+    H, k, E, R = 256, 2, 16, 4
     rng = np.random.default_rng(3)
     idx = rng.integers(0, E, (T, k))
     idx[123, 1] = E        # out of range
