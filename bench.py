@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+CAL_BYTES = 1 << 30  # size of the calibration kernels (elementwise copy, fill)
 METRIC = "dispatch+combine µs and achieved HBM GB/s at 8K tok, h7168, top-8, 1 GPU"
 
 
@@ -106,6 +107,78 @@ def cpu_baseline(workload_name, sample_tokens, min_seconds):
                       f"of {os.cpu_count()} host cores"}
 
 
+KERNEL_KEYS = {"combine": "combine_kernel", "dispatch": "dispatch_fp8_kernel",
+               "layout_count": "layout_count_kernel", "layout_scatter": "layout_scatter_kernel",
+               "layout_small": "layout_small_kernel"}
+CAL_COPY_KEY = "bitwise_not"      # elementwise kernel: reads and writes CAL_BYTES
+CAL_FILL_KEY = "FillFunctor<unsigned char>"  # writes CAL_BYTES
+
+
+def summarize(trace_dir, fetch_dir, write_dir, workload, command_prefix):
+    """Write the profiles/ summaries from rocprofv3 CSV output: per-kernel
+    durations (--kernel-trace --stats) and HBM bytes per launch (two --pmc
+    passes, FETCH_SIZE and WRITE_SIZE, in KiB, each scaled by what the same
+    counter reads for a calibration kernel of known size)."""
+    import csv
+    import glob
+
+    def one(d, suffix):
+        f = glob.glob(os.path.join(d, "*" + suffix))
+        assert len(f) == 1, (d, suffix, f)
+        return list(csv.DictReader(open(f[0])))
+
+    stats = one(trace_dir, "_kernel_stats.csv")
+    fetch = one(fetch_dir, "_counter_collection.csv")
+    write = one(write_dir, "_counter_collection.csv")
+
+    def per_kernel(rows, key):
+        v = [float(r["Counter_Value"]) for r in rows if key in r["Kernel_Name"]]
+        return statistics.median(v) if v else None
+
+    fetch_cal = per_kernel(fetch, CAL_COPY_KEY)     # KiB read by a CAL_BYTES-read kernel
+    write_cal = per_kernel(write, CAL_FILL_KEY)     # KiB written by a CAL_BYTES-write kernel
+    f_fetch = CAL_BYTES / fetch_cal
+    f_write = CAL_BYTES / write_cal
+    cmd_trace = f"{command_prefix} rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o {workload} -- python3 bench.py --config {workload} --steps 20 --warmup 3 --skip-cpu"
+    lines = [f"# Kernel durations and HBM traffic, {workload} workload", "",
+             "Kernel-trace command (run from the repository root):", "", "```", cmd_trace, "```", "",
+             "Counter commands (one pass each):", "", "```",
+             f"{command_prefix} rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o {workload} -- python3 bench.py --config {workload} --steps 3 --warmup 1 --skip-cpu",
+             f"{command_prefix} rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o {workload} -- python3 bench.py --config {workload} --steps 3 --warmup 1 --skip-cpu",
+             "```", "",
+             f"Counter calibration: FETCH_SIZE of the elementwise copy kernel ({CAL_BYTES} B read) = "
+             f"{fetch_cal:.0f} KiB, so FETCH bytes = FETCH_SIZE x {f_fetch:.4f}; WRITE_SIZE of the fill "
+             f"kernel ({CAL_BYTES} B written) = {write_cal:.0f} KiB, so WRITE bytes = WRITE_SIZE x {f_write:.4f}.", "",
+             "| kernel | calls | avg us | min us | max us | HBM read MB/launch | HBM write MB/launch |",
+             "|---|---|---|---|---|---|---|"]
+    traffic = {}
+    for short, key in KERNEL_KEYS.items():
+        st = [r for r in stats if key in r["Name"]]
+        if not st:
+            continue
+        r = st[0]
+        fr, wr = per_kernel(fetch, key), per_kernel(write, key)
+        rb = fr * f_fetch if fr is not None else None
+        wb = wr * f_write if wr is not None else None
+        traffic[short] = (rb, wb)
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | {float(r['MinNs'])/1e3:.2f} | "
+                     f"{float(r['MaxNs'])/1e3:.2f} | {rb/1e6 if rb else float('nan'):.1f} | {wb/1e6 if wb else float('nan'):.1f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    md = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    open(md, "w").write("\n".join(lines) + "\n")
+    for kernel in ("combine", "dispatch"):
+        if kernel in traffic and traffic[kernel][0] is not None:
+            rec = {"kernel": kernel, "workload": workload,
+                   "source_sha": source_sha(kernel_sources()[kernel]),
+                   "hbm_read_bytes_per_launch": round(traffic[kernel][0]),
+                   "hbm_write_bytes_per_launch": round(traffic[kernel][1]),
+                   "hbm_bytes_per_launch": round(traffic[kernel][0] + traffic[kernel][1]),
+                   "fetch_scale": f_fetch, "write_scale": f_write, "summary": os.path.basename(md)}
+            json.dump(rec, open(os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json"), "w"),
+                      indent=1)
+    print(open(md).read())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,7 +189,15 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--num-workgroups", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph and replayed")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 CSV directories and exit")
+    ap.add_argument("--command-prefix", default="", help="recorded in the summary (e.g. env settings)")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(*args.summarize, args.config, args.command_prefix)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the expert-parallel ranks are simulated as "
@@ -184,22 +265,28 @@ def main():
         st = L.ep_combine(pc, ph, idx.data_ptr(), ry, wts.data_ptr(), out.data_ptr(), cap, sp)
         assert st == 0, st
 
-    # plain copy ceiling (1 GiB read + 1 GiB write), same run
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # Plain streaming kernels of known size, same run: an elementwise pass that
+    # reads 1 GiB and writes 1 GiB (the copy ceiling) and a 1 GiB fill (the
+    # write ceiling).  They are also the calibration kernels for the HBM byte
+    # counters (see --summarize).
+    src = torch.empty(CAL_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    src.fill_(1)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    cms = []
-    for _ in range(5):
-        e0.record()
-        dst.copy_(src)
-        e1.record()
-        e1.synchronize()
-        cms.append(e0.elapsed_time(e1))
-    copy_gbps = 2 * src.numel() / (statistics.median(cms) * 1e-3) / 1e9
+
+    def timed(fn, reps=5):
+        ms = []
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return statistics.median(ms)
+
+    fill_ms = timed(lambda: src.fill_(1))
+    copy_ms = timed(lambda: torch.bitwise_not(src, out=dst))
+    copy_gbps = 2 * CAL_BYTES / (copy_ms * 1e-3) / 1e9
+    write_gbps = CAL_BYTES / (fill_ms * 1e-3) / 1e9
     del src, dst
 
     for _ in range(args.warmup):
@@ -239,6 +326,31 @@ def main():
         s = sorted(v)
         return round(s[min(len(s) - 1, int(q * len(s)))], 2)
 
+    graph_us = None
+    if args.graph:
+        # one step (layout + dispatch + combine) captured once, replayed K times
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        gsp = gs.cuda_stream
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g, stream=gs):
+                assert L.ep_layout(pc, idx.data_ptr(), ph, ws.data_ptr(), gsp) == 0
+                assert L.ep_dispatch(pc, ph, idx.data_ptr(), x.data_ptr(), rx, rs, cap, gsp) == 0
+                assert L.ep_combine(pc, ph, idx.data_ptr(), ry, wts.data_ptr(), out.data_ptr(), cap, gsp) == 0
+        stream.wait_stream(gs)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record()
+        for _ in range(K):
+            g.replay()
+        gb.record()
+        torch.cuda.synchronize()
+        graph_us = ga.elapsed_time(gb) * 1e3 / K
+        assert int(h.error_flag.item()) == 0
+
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -269,7 +381,9 @@ def main():
         "dispatch_GBps": round(b["dispatch"] / (statistics.median(dis) * 1e-6) / 1e9, 1),
         "combine_GBps": round(b["combine"] / (statistics.median(com) * 1e-6) / 1e9, 1),
         "copy_ceiling_GBps": round(copy_gbps, 1),
+        "write_ceiling_GBps": round(write_gbps, 1),
         "bytes_per_step": step_bytes,
+        "graph_step_us": None if graph_us is None else round(graph_us, 2),
         "cpu_baseline": None,
     }
     if not args.skip_cpu:
