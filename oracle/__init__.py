@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_quantize_row.argtypes = [i32, vp, vp, vp]
         L.oracle_unpermute.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.oracle_combine_shared.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_combine_backward.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
@@ -234,6 +236,46 @@ def combine(recv_y, topk_idx: np.ndarray, L: Layout, weights=None) -> np.ndarray
     lib().oracle_combine(L.T, H, L.k, L.E, L.R, _p(idx), _p(L.slot_of), _p(L.rank_offsets),
                          _ptr_array(ys), wp, _p(out))
     return out
+
+
+def _weights_or_none(weights):
+    return None if weights is None else np.ascontiguousarray(weights, dtype=np.float32)
+
+
+def combine_shared(recv_y, topk_idx: np.ndarray, L: Layout, weights, shared: np.ndarray) -> np.ndarray:
+    """Weighted combine with the shared expert's output added last (see
+    ep_oracle.h)."""
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    H = recv_y[0].shape[1]
+    ys = [np.ascontiguousarray(r, dtype=np.uint16) for r in _rows_or_empty(recv_y, H)]
+    sh = np.ascontiguousarray(shared, dtype=np.uint16)
+    assert sh.shape == (L.T, H)
+    w = _weights_or_none(weights)
+    out = np.empty((L.T, H), np.uint16)
+    lib().oracle_combine_shared(L.T, H, L.k, L.E, L.R, _p(idx), _p(L.slot_of), _p(L.rank_offsets),
+                                _ptr_array(ys), None if w is None else _p(w), _p(sh), _p(out))
+    return out
+
+
+def combine_backward(grad_out: np.ndarray, topk_idx: np.ndarray, L: Layout, weights=None,
+                     recv_y=None):
+    """Backward of combine: (grad_recv, grad_w).  grad_recv is R arrays
+    [rank_counts[r], H] uint16; grad_w is [T, k] float32, or None when
+    recv_y is None."""
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    g = np.ascontiguousarray(grad_out, dtype=np.uint16)
+    T, H = g.shape
+    gr = [np.empty((int(L.rank_counts[r]), H), np.uint16) for r in range(L.R)]
+    w = _weights_or_none(weights)
+    ys = None if recv_y is None else [np.ascontiguousarray(r, dtype=np.uint16)
+                                      for r in _rows_or_empty(recv_y, H)]
+    gw = None if recv_y is None else np.empty((T, L.k), np.float32)
+    lib().oracle_combine_backward(T, H, L.k, L.E, L.R, _p(idx), _p(L.slot_of), _p(L.rank_offsets),
+                                  _p(g), None if w is None else _p(w),
+                                  None if ys is None else _ptr_array(ys),
+                                  _ptr_array(_rows_or_empty(gr, H)),
+                                  None if gw is None else _p(gw))
+    return gr, gw
 
 
 def dequant_identity_expert(recv_q, recv_s):

@@ -306,3 +306,63 @@ void oracle_combine(int T, int H, int k, int E, int R, const int32_t *idx,
     }
     free(rows);
 }
+
+void oracle_combine_shared(int T, int H, int k, int E, int R, const int32_t *idx,
+                           const int32_t *slot, const int32_t *roff,
+                           const uint16_t *const *recv_y, const float *w,
+                           const uint16_t *shared, uint16_t *out)
+{
+    const int El = E / R;
+    (void)R;
+    const uint16_t **rows = (const uint16_t **)malloc((size_t)k * sizeof(*rows));
+    if (!rows)
+        return;
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int64_t p = (int64_t)t * k + j;
+            int r = idx[p] / El;
+            rows[j] = recv_y[r] + (int64_t)(slot[p] - roff[r]) * H;
+        }
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                float wj = w ? w[(int64_t)t * k + j] : 1.0f;
+                acc = fmaf(wj, oracle_bf16_to_f32(rows[j][h]), acc);
+            }
+            acc = acc + oracle_bf16_to_f32(shared[(int64_t)t * H + h]);
+            out[(int64_t)t * H + h] = oracle_bf16_rne(acc);
+        }
+    }
+    free(rows);
+}
+
+void oracle_combine_backward(int T, int H, int k, int E, int R, const int32_t *idx,
+                             const int32_t *slot, const int32_t *roff,
+                             const uint16_t *grad_out, const float *w,
+                             const uint16_t *const *recv_y, uint16_t *const *grad_recv,
+                             float *grad_w)
+{
+    const int El = E / R;
+    (void)R;
+    for (int t = 0; t < T; ++t) {
+        const uint16_t *g = grad_out + (int64_t)t * H;
+        for (int j = 0; j < k; ++j) {
+            int64_t p = (int64_t)t * k + j;
+            int r = idx[p] / El;
+            int64_t rrow = slot[p] - roff[r];
+            float wj = w ? w[p] : 1.0f;
+            uint16_t *dst = grad_recv[r] + rrow * H;
+            for (int h = 0; h < H; ++h) {
+                float prod = wj * oracle_bf16_to_f32(g[h]); /* one binary32 multiply */
+                dst[h] = oracle_bf16_rne(prod);
+            }
+            if (grad_w) {
+                const uint16_t *y = recv_y[r] + rrow * H;
+                double dot = 0.0;
+                for (int h = 0; h < H; ++h)
+                    dot += (double)oracle_bf16_to_f32(g[h]) * (double)oracle_bf16_to_f32(y[h]);
+                grad_w[p] = (float)dot;
+            }
+        }
+    }
+}

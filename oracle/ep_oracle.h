@@ -78,6 +78,27 @@ void oracle_combine(int T, int H, int k, int E, int R, const int32_t *idx,
                     const int32_t *slot, const int32_t *roff,
                     const uint16_t *const *recv_y, const float *w, uint16_t *out);
 
+/* Weighted combine plus the shared expert ([Perplexity blog], "Sérfræðinga-
+ * samsíðun": every token also runs through the shared expert and that result
+ * is added to the routed experts' result): acc as in oracle_combine, then
+ * acc = acc + f32(shared[t][h]) (one binary32 addition), then bf16 RNE. */
+void oracle_combine_shared(int T, int H, int k, int E, int R, const int32_t *idx,
+                           const int32_t *slot, const int32_t *roff,
+                           const uint16_t *const *recv_y, const float *w,
+                           const uint16_t *shared, uint16_t *out);
+
+/* Backward of combine ([DeepEP overview], "Pola penggunaan ...": the backward
+ * of combine is a dispatch).  For every pair p = (t, j):
+ *   grad_recv[r][row(p)][h] = BF16_RNE(RN32(w[p] * f32(grad_out[t][h])))
+ *     (w == NULL: unit weights, an exact copy), and, when grad_w != NULL,
+ *   grad_w[p] = RN32( sum_h f32(grad_out[t][h]) * f32(y[r][row(p)][h]) ),
+ *     the sum taken in binary64 (each bf16 x bf16 product is exact there). */
+void oracle_combine_backward(int T, int H, int k, int E, int R, const int32_t *idx,
+                             const int32_t *slot, const int32_t *roff,
+                             const uint16_t *grad_out, const float *w,
+                             const uint16_t *const *recv_y, uint16_t *const *grad_recv,
+                             float *grad_w);
+
 /* Codecs. */
 uint8_t  oracle_e4m3_encode(float v);
 float    oracle_e4m3_decode(uint8_t c);
