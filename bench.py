@@ -47,6 +47,17 @@ def algorithmic_bytes(T, H, k, E, R, fp8):
     return dict(layout=layout, dispatch=dispatch, combine=combine)
 
 
+def extra_bytes(T, H, k):
+    """Algorithmic bytes of the entry points outside the forward step."""
+    P = T * k
+    return {
+        # combine plus reading the shared expert's [T,H] bf16 rows
+        "combine_shared": 2 * H * P + 2 * H * T + 2 * H * T + 12 * P,
+        # read grad_out, read y, write the gradient rows, read w/idx/slot, write grad_w
+        "combine_backward": 2 * H * T + 2 * H * P + 2 * H * P + 12 * P + 4 * P,
+    }
+
+
 def source_sha(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -189,6 +200,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--num-workgroups", type=int, default=0)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip timing combine_shared and combine_backward")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph and replayed")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -326,6 +339,41 @@ def main():
         s = sorted(v)
         return round(s[min(len(s) - 1, int(q * len(s)))], 2)
 
+    extras = None
+    if not args.no_extras:
+        # the other entry points on the same handle and buffers: combine with a
+        # shared-expert row, and the backward of combine (gradient rows + grad_w)
+        gen.manual_seed(2)
+        shared = torch.randn((w.T, w.H), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+        gout = torch.randn((w.T, w.H), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+        grows = [torch.empty((cap, w.H), dtype=torch.int16, device=dev) for _ in range(w.R)]
+        gwt = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+        rgp = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in grows])
+        xb = extra_bytes(w.T, w.H, w.k)
+        calls = {
+            "combine_shared": lambda: L.ep_combine_shared(pc, ph, idx.data_ptr(), ry, wts.data_ptr(),
+                                                          shared.data_ptr(), out.data_ptr(), cap, sp),
+            "combine_backward": lambda: L.ep_combine_backward(pc, ph, idx.data_ptr(), gout.data_ptr(),
+                                                              wts.data_ptr(), ry, rgp, gwt.data_ptr(),
+                                                              cap, sp),
+        }
+        extras = {}
+        for name, fn in calls.items():
+            for _ in range(3):
+                assert fn() == 0
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(min(K, 20))]
+            for a, b_ in evs:
+                a.record(stream)
+                assert fn() == 0
+                b_.record(stream)
+            torch.cuda.synchronize()
+            us = statistics.median(a.elapsed_time(b_) * 1e3 for a, b_ in evs)
+            extras[name] = {"us": round(us, 2), "algorithmic_bytes": xb[name],
+                            "GBps": round(xb[name] / (us * 1e-6) / 1e9, 1)}
+        assert int(h.error_flag.item()) == 0
+        del shared, gout, grows, gwt
+
     graph_us = None
     if args.graph:
         # one step (layout + dispatch + combine) captured once, replayed K times
@@ -384,6 +432,7 @@ def main():
         "write_ceiling_GBps": round(write_gbps, 1),
         "bytes_per_step": step_bytes,
         "graph_step_us": None if graph_us is None else round(graph_us, 2),
+        "extras": extras,
         "cpu_baseline": None,
     }
     if not args.skip_cpu:

@@ -23,7 +23,7 @@ EP_MAX_RANKS, EP_MAX_TOPK, EP_MAX_EXPERTS, EP_MAX_HIDDEN = 64, 32, 2048, 65536
 # Every symbol include/ep.h declares.
 EXPORTS = ("ep_abi_version", "ep_status_string", "ep_recv_capacity_rows",
            "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine",
-           "ep_unpermute")
+           "ep_combine_shared", "ep_combine_backward", "ep_unpermute")
 
 
 class EpError(RuntimeError):
@@ -76,6 +76,11 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.ep_dispatch.argtypes = [cfgp, hp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, vp]
     L.ep_combine.restype = ctypes.c_int32
     L.ep_combine.argtypes = [cfgp, hp, vp, ctypes.POINTER(vp), vp, vp, i64, vp]
+    L.ep_combine_shared.restype = ctypes.c_int32
+    L.ep_combine_shared.argtypes = [cfgp, hp, vp, ctypes.POINTER(vp), vp, vp, vp, i64, vp]
+    L.ep_combine_backward.restype = ctypes.c_int32
+    L.ep_combine_backward.argtypes = [cfgp, hp, vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                      vp, i64, vp]
     L.ep_unpermute.restype = ctypes.c_int32
     L.ep_unpermute.argtypes = [cfgp, hp, vp, ctypes.POINTER(vp), vp, i64, vp]
     return L
@@ -169,6 +174,24 @@ def ep_combine(cfg, handle, topk_idx, recv_y, topk_weights, out, capacity_rows, 
     _check(load().ep_combine(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)), _ptr(topk_idx),
                              _ptrs(recv_y), _ptr(topk_weights), _ptr(out), int(capacity_rows),
                              _stream(stream)), "ep_combine")
+
+
+def ep_combine_shared(cfg, handle, topk_idx, recv_y, topk_weights, shared, out, capacity_rows,
+                      stream=None) -> None:
+    _check(load().ep_combine_shared(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)),
+                                    _ptr(topk_idx), _ptrs(recv_y), _ptr(topk_weights), _ptr(shared),
+                                    _ptr(out), int(capacity_rows), _stream(stream)),
+           "ep_combine_shared")
+
+
+def ep_combine_backward(cfg, handle, topk_idx, grad_out, topk_weights, recv_y, grad_recv,
+                        grad_weights, capacity_rows, stream=None) -> None:
+    ry = None if recv_y is None else _ptrs(recv_y)
+    _check(load().ep_combine_backward(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)),
+                                      _ptr(topk_idx), _ptr(grad_out), _ptr(topk_weights), ry,
+                                      _ptrs(grad_recv), _ptr(grad_weights), int(capacity_rows),
+                                      _stream(stream)),
+           "ep_combine_backward")
 
 
 def ep_unpermute(cfg, handle, topk_idx, recv_y, out, capacity_rows, stream=None) -> None:

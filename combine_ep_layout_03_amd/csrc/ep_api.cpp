@@ -124,8 +124,48 @@ ep_status ep_combine(const ep_config *cfg, const ep_layout_t *h, const int32_t *
     ry.p[r] = recv_y[r];
   }
   trace("combine", cfg, ep::row_grid(*cfg, cfg->num_tokens));
-  return from_hip(
-      ep::launch_combine(*cfg, *h, topk_idx, ry, topk_weights, out, capacity_rows, stream));
+  return from_hip(ep::launch_combine(*cfg, *h, topk_idx, ry, topk_weights, nullptr, out,
+                                     capacity_rows, stream));
+}
+
+ep_status ep_combine_shared(const ep_config *cfg, const ep_layout_t *h, const int32_t *topk_idx,
+                            const void *const *recv_y, const float *topk_weights,
+                            const void *shared, void *out, int64_t capacity_rows,
+                            hipStream_t stream) {
+  ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
+  if (st != EP_OK) return st;
+  if (!recv_y || !out || !shared) return EP_ERR_INVALID_ARG;
+  ep::RankCPtrs ry{};
+  for (int r = 0; r < cfg->num_ranks; ++r) {
+    if (!recv_y[r]) return EP_ERR_INVALID_ARG;
+    ry.p[r] = recv_y[r];
+  }
+  trace("combine_shared", cfg, ep::row_grid(*cfg, cfg->num_tokens));
+  return from_hip(ep::launch_combine(*cfg, *h, topk_idx, ry, topk_weights, shared, out,
+                                     capacity_rows, stream));
+}
+
+ep_status ep_combine_backward(const ep_config *cfg, const ep_layout_t *h, const int32_t *topk_idx,
+                              const void *grad_out, const float *topk_weights,
+                              const void *const *recv_y, void *const *grad_recv,
+                              float *grad_weights, int64_t capacity_rows, hipStream_t stream) {
+  ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
+  if (st != EP_OK) return st;
+  if (!grad_out || !grad_recv) return EP_ERR_INVALID_ARG;
+  if ((recv_y == nullptr) != (grad_weights == nullptr)) return EP_ERR_INVALID_ARG;
+  ep::RankCPtrs ry{};
+  ep::RankPtrs rg{};
+  for (int r = 0; r < cfg->num_ranks; ++r) {
+    if (!grad_recv[r]) return EP_ERR_INVALID_ARG;
+    rg.p[r] = grad_recv[r];
+    if (recv_y) {
+      if (!recv_y[r]) return EP_ERR_INVALID_ARG;
+      ry.p[r] = recv_y[r];
+    }
+  }
+  trace("combine_backward", cfg, ep::row_grid(*cfg, cfg->num_tokens));
+  return from_hip(ep::launch_combine_backward(*cfg, *h, topk_idx, grad_out, topk_weights, ry, rg,
+                                              grad_weights, capacity_rows, stream));
 }
 
 ep_status ep_unpermute(const ep_config *cfg, const ep_layout_t *h, const int32_t *topk_idx,

@@ -54,6 +54,15 @@ __device__ inline void fma8(float *acc, float w, u32x4 v) {
   }
 }
 
+// acc[0..7] += (8 bf16 of v), one binary32 addition each.
+__device__ inline void add8(float *acc, u32x4 v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] = acc[2 * i] + __uint_as_float(v[i] << 16);
+    acc[2 * i + 1] = acc[2 * i + 1] + __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+
 __device__ inline u32x4 pack8(const float *acc) {
   u32x4 o;
 #pragma unroll
@@ -78,11 +87,15 @@ __device__ inline uint64_t src_row(const int32_t *__restrict__ idx,
   return 0;
 }
 
+// HasShared: the shared expert's row is added after the routed fold
+// ([Perplexity blog], "Sérfræðinga-samsíðun": every token also runs through
+// the shared expert, whose result is added to the routed experts' result).
+template <bool HasShared>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ slot_of,
     const int32_t *__restrict__ rank_offsets, int32_t *__restrict__ err,
     const float *__restrict__ w, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El,
-    int64_t cap, RankCPtrs ry, uint16_t *__restrict__ out) {
+    int64_t cap, RankCPtrs ry, const uint16_t *__restrict__ shared, uint16_t *__restrict__ out) {
   if (*err != 0) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int nch = H / 8;
@@ -104,6 +117,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     float acc0[8], acc1[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc0[i] = acc1[i] = 0.0f;
+    u32x4 sh0 = {0u, 0u, 0u, 0u}, sh1 = {0u, 0u, 0u, 0u};
+    if (HasShared) {
+      const u32x4 *srow = reinterpret_cast<const u32x4 *>(shared + t * H);
+      if (ok0) sh0 = __builtin_nontemporal_load(srow + c0);
+      if (ok1) sh1 = __builtin_nontemporal_load(srow + c1);
+    }
     for (int j0 = 0; j0 < k; j0 += kJB) {
       u32x4 v0[kJB], v1[kJB];
 #pragma unroll
@@ -123,9 +142,101 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
         }
       }
     }
+    if (HasShared) {
+      add8(acc0, sh0);
+      add8(acc1, sh1);
+    }
     u32x4 *orow = reinterpret_cast<u32x4 *>(out + t * H);
     if (ok0) __builtin_nontemporal_store(pack8(acc0), orow + c0);
     if (ok1) __builtin_nontemporal_store(pack8(acc1), orow + c1);
+  }
+}
+
+// Backward of combine ([DeepEP overview], "Pola penggunaan ...": the backward
+// of combine is a dispatch).  One wave per token (grid-stride); the k pairs
+// are taken in blocks of 8: for each block the wave streams the token's
+// grad_out row once, writes bf16(RN32(w_j * g)) into each pair's gradient row
+// and, when y is given, accumulates each pair's dot product <g, y_j> per lane
+// (fp32 fma over the lane's channels in order), then reduces it across the
+// wave with a fixed xor-butterfly, so the result is deterministic.
+__global__ __launch_bounds__(kThreads) void combine_backward_kernel(
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ slot_of,
+    const int32_t *__restrict__ rank_offsets, int32_t *__restrict__ err,
+    const uint16_t *__restrict__ gout, const float *__restrict__ w, int32_t T, int32_t H,
+    int32_t k, int32_t E, int32_t El, int64_t cap, RankCPtrs ry, RankPtrs rg,
+    float *__restrict__ gw) {
+  if (*err != 0) return;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int nch = H / 8;
+  const bool want_w = gw != nullptr;
+  for (int64_t t = (int64_t)blockIdx.x * kRowWaves + wave; t < T;
+       t += (int64_t)gridDim.x * kRowWaves) {
+    uint64_t dst = 0, src = 0;
+    float wj = 0.0f;
+    if (lane < k) {
+      const int64_t p = t * k + lane;
+      const int32_t e = idx[p];
+      if ((uint32_t)e < (uint32_t)E) {
+        const int32_t r = e / El;
+        const int64_t rr = (int64_t)slot_of[p] - rank_offsets[r];
+        if (rr >= 0 && rr < cap) {
+          dst = (uint64_t)rg.p[r] + (uint64_t)(rr * (int64_t)H * 2);
+          if (want_w) src = (uint64_t)ry.p[r] + (uint64_t)(rr * (int64_t)H * 2);
+        }
+      }
+      if (dst == 0) atomicOr(err, (int32_t)EP_DEVERR_ROW);
+      wj = w ? w[p] : 1.0f;
+    }
+    if (__ballot(lane < k && dst == 0) != 0) continue;  // a bad row: write nothing for t
+    const u32x4 *grow = reinterpret_cast<const u32x4 *>(gout + t * H);
+    for (int j0 = 0; j0 < k; j0 += kJB) {
+      float acc[kJB];
+#pragma unroll
+      for (int jj = 0; jj < kJB; ++jj) acc[jj] = 0.0f;
+      for (int c = lane; c < nch; c += kWave) {
+        const u32x4 g = grow[c];
+        u32x4 v[kJB];
+        if (want_w) {
+#pragma unroll
+          for (int jj = 0; jj < kJB; ++jj)
+            if (j0 + jj < k)
+              v[jj] = __builtin_nontemporal_load(
+                  reinterpret_cast<const u32x4 *>(readlane64(src, j0 + jj)) + c);
+        }
+#pragma unroll
+        for (int jj = 0; jj < kJB; ++jj) {
+          if (j0 + jj < k) {
+            const float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j0 + jj));
+            float prod[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              prod[2 * i] = wv * __uint_as_float(g[i] << 16);
+              prod[2 * i + 1] = wv * __uint_as_float(g[i] & 0xFFFF0000u);
+            }
+            u32x4 *drow = reinterpret_cast<u32x4 *>(readlane64(dst, j0 + jj));
+            __builtin_nontemporal_store(pack8(prod), drow + c);
+            if (want_w) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                acc[jj] = __builtin_fmaf(__uint_as_float(g[i] << 16),
+                                         __uint_as_float(v[jj][i] << 16), acc[jj]);
+                acc[jj] = __builtin_fmaf(__uint_as_float(g[i] & 0xFFFF0000u),
+                                         __uint_as_float(v[jj][i] & 0xFFFF0000u), acc[jj]);
+              }
+            }
+          }
+        }
+      }
+      if (want_w) {
+#pragma unroll
+        for (int jj = 0; jj < kJB; ++jj) {
+          float a = acc[jj];
+#pragma unroll
+          for (int o = kWave / 2; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+          if (lane == 0 && j0 + jj < k) gw[t * k + j0 + jj] = a;
+        }
+      }
+    }
   }
 }
 
@@ -151,14 +262,34 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(
 }  // namespace
 
 hipError_t launch_combine(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
-                          const RankCPtrs &ry, const float *w, void *out, int64_t capacity_rows,
-                          hipStream_t s) {
+                          const RankCPtrs &ry, const float *w, const void *shared, void *out,
+                          int64_t capacity_rows, hipStream_t s) {
   const int64_t nseg = (c.hidden / 8 + kSegChunks - 1) / kSegChunks;
   const int grid = row_grid(c, (int64_t)c.num_tokens * nseg);
-  hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kThreads), 0, s, topk_idx, h.slot_of,
-                     h.rank_offsets, h.error_flag, w, c.num_tokens, c.hidden, c.num_topk,
-                     c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,
-                     static_cast<uint16_t *>(out));
+  if (shared) {
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(kThreads), 0, s, topk_idx, h.slot_of,
+                       h.rank_offsets, h.error_flag, w, c.num_tokens, c.hidden, c.num_topk,
+                       c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,
+                       static_cast<const uint16_t *>(shared), static_cast<uint16_t *>(out));
+  } else {
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(kThreads), 0, s, topk_idx,
+                       h.slot_of, h.rank_offsets, h.error_flag, w, c.num_tokens, c.hidden,
+                       c.num_topk, c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,
+                       nullptr, static_cast<uint16_t *>(out));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_backward(const ep_config &c, const ep_layout_t &h,
+                                   const int32_t *topk_idx, const void *grad_out, const float *w,
+                                   const RankCPtrs &ry, const RankPtrs &rg, float *grad_w,
+                                   int64_t capacity_rows, hipStream_t s) {
+  const int grid = row_grid(c, c.num_tokens);
+  hipLaunchKernelGGL(combine_backward_kernel, dim3(grid), dim3(kThreads), 0, s, topk_idx,
+                     h.slot_of, h.rank_offsets, h.error_flag,
+                     static_cast<const uint16_t *>(grad_out), w, c.num_tokens, c.hidden,
+                     c.num_topk, c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,
+                     rg, grad_w);
   return hipGetLastError();
 }
 

@@ -53,8 +53,13 @@ hipError_t launch_dispatch(const ep_config &c, const ep_layout_t &h, const int32
                            int64_t capacity_rows, hipStream_t s);
 
 hipError_t launch_combine(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
-                          const RankCPtrs &ry, const float *w, void *out, int64_t capacity_rows,
-                          hipStream_t s);
+                          const RankCPtrs &ry, const float *w, const void *shared, void *out,
+                          int64_t capacity_rows, hipStream_t s);
+
+hipError_t launch_combine_backward(const ep_config &c, const ep_layout_t &h,
+                                   const int32_t *topk_idx, const void *grad_out, const float *w,
+                                   const RankCPtrs &ry, const RankPtrs &rg, float *grad_w,
+                                   int64_t capacity_rows, hipStream_t s);
 
 hipError_t launch_unpermute(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
                             const RankCPtrs &ry, void *out, int64_t capacity_rows, hipStream_t s);

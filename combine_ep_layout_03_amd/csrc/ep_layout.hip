@@ -327,7 +327,6 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
   int32_t *misc = base + kLayoutWaves * E;   // [kLayoutWaves] scan scratch, [kLayoutWaves] bad counts
   int32_t *stage = lds + ((E + 1) + kLayoutWaves * E + 8 + 3) / 4 * 4;  // [kLayoutWaves][kStage], 16-byte aligned
   const int tid = threadIdx.x, wave = tid / kWave;
-  const int E1 = E + 1;
   const int64_t c0 = (int64_t)blockIdx.x * kLayoutWaves;
 
   // Row e of the table holds expert e's count in every chunk: sum it for the

@@ -178,6 +178,35 @@ ep_status ep_combine(const ep_config *cfg /*(host)*/, const ep_layout_t *h /*(ho
                      const float *topk_weights, void *out, int64_t capacity_rows,
                      hipStream_t stream);
 
+/* Combine plus the shared expert ([Perplexity blog] "Sérfræðinga-samsíðun":
+ * every token also goes through the shared expert, whose result is added to
+ * the routed experts' result).  As ep_combine, except that after the routed
+ * fold acc = acc + f32(shared[t][h]) (one fp32 addition) before the bf16
+ * rounding.  shared is [T,H] bf16 and must not be NULL. */
+ep_status ep_combine_shared(const ep_config *cfg /*(host)*/, const ep_layout_t *h /*(host)*/,
+                            const int32_t *topk_idx, const void *const *recv_y /*(host)[R]*/,
+                            const float *topk_weights, const void *shared, void *out,
+                            int64_t capacity_rows, hipStream_t stream);
+
+/* Backward of combine ([DeepEP overview] "Pola penggunaan ...": the backward
+ * of combine is a dispatch).  For every pair p = (t, j) with its row as in
+ * ep_combine:
+ *   grad_recv[r] row `row` (H bf16) := bf16(w[t][j] * grad_out[t][h]), the
+ *     product one fp32 multiply, rounded to nearest even (topk_weights NULL:
+ *     unit weights, an exact copy);
+ *   grad_weights[t][j] := <grad_out[t], y row>, accumulated in fp32 (each
+ *     lane's channels in order, then a fixed butterfly across the wave), when
+ *     recv_y / grad_weights are given; pass both or neither.
+ * The backward of dispatch is ep_combine with topk_weights NULL applied to
+ * the gradient rows.  grad_out is [T,H] bf16; grad_recv and recv_y are (host)
+ * arrays of R device pointers to [capacity_rows, H] bf16; grad_weights is
+ * [T,k] fp32. */
+ep_status ep_combine_backward(const ep_config *cfg /*(host)*/, const ep_layout_t *h /*(host)*/,
+                              const int32_t *topk_idx, const void *grad_out,
+                              const float *topk_weights, const void *const *recv_y /*(host)[R]*/,
+                              void *const *grad_recv /*(host)[R]*/, float *grad_weights,
+                              int64_t capacity_rows, hipStream_t stream);
+
 /* Un-permute ([torchtitan PR]: the token unpermute after the experts) as a
  * standalone call for testing: out[p] (H bf16) := recv_y[r(p)] row row(p), so
  * out is [T*k, H] in (t, j) order.  Same arguments and errors as ep_combine. */

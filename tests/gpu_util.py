@@ -116,3 +116,15 @@ def rel_err(g_bits: np.ndarray, r_bits: np.ndarray) -> float:
     g = (g_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     r = (r_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return float(np.max(np.abs(g - r) / np.maximum(np.abs(r), 1e-3))) if g.size else 0.0
+
+
+def rows_to_dev(cap, H, rows_np):
+    """R capacity-sized bf16 device buffers holding the given valid rows."""
+    bufs = []
+    for y in rows_np:
+        b = torch.empty((cap, H), dtype=torch.int16, device=DEV)
+        b.view(torch.uint8).fill_(POISON)
+        if y.shape[0]:
+            b[:y.shape[0]] = to_dev(y)
+        bufs.append(b)
+    return bufs

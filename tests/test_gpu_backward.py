@@ -1,0 +1,123 @@
+"""GPU parity of the combine-with-shared-expert and combine-backward entry
+points against the oracle, through the C ABI.
+
+Bar: combine_shared within the 1e-2 combine tolerance (bit mismatches
+reported); grad_recv rows bit-exact (one fp32 multiply, then bf16 nearest
+even, on both sides); grad_weights within 1e-5 * sum_h |g_h y_h| of the
+oracle's float64 dot product (the fp32 accumulation of a lane's channels
+plus a 64-lane butterfly is bounded by ~120 * 2^-24 of that sum).
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_layout_03_amd as ep
+import oracle
+from workloads import CONFIGS, make_workload, make_expert_rows, bf16_from_f32
+
+from gpu_util import GpuRun, POISON, rel_err, rows_to_dev, say, u16, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ep.load()
+
+
+def prep(name, T=None):
+    w = make_workload(name, T=T)
+    run = GpuRun(w).layout()
+    L = oracle.layout(w.topk_idx, w.E, w.R)
+    y = make_expert_rows(w.P, w.H)
+    ys = [y[L.rank_offsets[r]:L.rank_offsets[r + 1]] for r in range(w.R)]
+    return w, run, L, ys
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_combine_shared_full_configs(name):
+    w, run, L, ys = prep(name)
+    say(f"combine_shared {name}")
+    shared = bf16_from_f32(np.random.default_rng(3).standard_normal((w.T, w.H)).astype(np.float32))
+    run.put_expert_rows(ys)
+    out = torch.empty((w.T, w.H), dtype=torch.int16, device="cuda")
+    ep.ep_combine_shared(run.cfg, run.h, run.idx, run.ybufs, run.wts, to_dev(shared), out, run.cap)
+    torch.cuda.synchronize()
+    ref = oracle.combine_shared(ys, w.topk_idx, L, w.topk_w, shared)
+    got = u16(out)
+    say(f"  max rel err {rel_err(got, ref):.3g}, bit mismatches {int(np.count_nonzero(got != ref))}")
+    assert rel_err(got, ref) <= 1e-2
+    assert np.array_equal(got, ref)
+
+
+def check_backward(w, run, L, ys, weights=True, with_w=True):
+    rng = np.random.default_rng(11)
+    g = bf16_from_f32(rng.standard_normal((w.T, w.H)).astype(np.float32))
+    grad_rows = rows_to_dev(run.cap, w.H, [np.zeros((0, w.H), np.uint16)] * w.R)
+    ybufs = rows_to_dev(run.cap, w.H, ys) if with_w else None
+    gw = torch.full((w.T, w.k), float("nan"), dtype=torch.float32, device="cuda") if with_w else None
+    ep.ep_combine_backward(run.cfg, run.h, run.idx, to_dev(g), run.wts if weights else None, ybufs,
+                           grad_rows, gw, run.cap)
+    torch.cuda.synchronize()
+    ref_rows, ref_gw = oracle.combine_backward(g, w.topk_idx, L, w.topk_w if weights else None,
+                                               ys if with_w else None)
+    for r in range(w.R):
+        n = int(L.rank_counts[r])
+        got = grad_rows[r].cpu().numpy().view(np.uint16)
+        assert np.array_equal(got[:n], ref_rows[r]), f"rank {r}"
+        assert np.all(got[n:].view(np.uint8) == POISON)
+    if with_w:
+        got_w = gw.cpu().numpy()
+        yrow = oracle.bf16_to_f32(np.concatenate(ys)[L.slot_of]).astype(np.float64).reshape(w.T, w.k, w.H)
+        mag = np.einsum("th,tkh->tk", np.abs(oracle.bf16_to_f32(g).astype(np.float64)), np.abs(yrow))
+        err = np.abs(got_w.astype(np.float64) - ref_gw.astype(np.float64))
+        say(f"  grad_w max err / sum|gy| = {float(np.max(err / np.maximum(mag, 1e-30))):.3g}")
+        assert np.all(err <= 1e-5 * mag + 1e-30)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ds16b", "decode", "v3"])
+def test_combine_backward_full_configs(name):
+    w, run, L, ys = prep(name)
+    say(f"combine_backward {name}")
+    check_backward(w, run, L, ys)
+
+
+def test_combine_backward_unit_weights_no_grad_w():
+    w, run, L, ys = prep("ds16b", T=777)
+    say("combine_backward unit weights, no grad_w")
+    check_backward(w, run, L, ys, weights=False, with_w=False)
+
+
+@pytest.mark.parametrize("T,H,k,E,R", [(1, 8, 1, 1, 1), (33, 264, 9, 18, 6), (70, 512, 32, 64, 8)])
+def test_combine_backward_small_ragged(T, H, k, E, R):
+    from test_gpu_parity import custom
+    rng = np.random.default_rng(T + k)
+    w = custom("bw", T, H, k, E, R, False, rng.integers(0, E, (T, k)), seed=T)
+    run = GpuRun(w).layout()
+    L = oracle.layout(w.topk_idx, w.E, w.R)
+    y = make_expert_rows(w.P, w.H)
+    ys = [y[L.rank_offsets[r]:L.rank_offsets[r + 1]] for r in range(w.R)]
+    say(f"combine_backward small T={T} H={H} k={k}")
+    check_backward(w, run, L, ys)
+
+
+def test_dispatch_backward_is_unit_weight_combine():
+    """The backward of dispatch: sum each token's k gradient rows (ep_combine
+    with unit weights) equals the oracle's unit-weight combine."""
+    w, run, L, ys = prep("ds16b", T=1000)
+    say("dispatch backward")
+    run.put_expert_rows(ys).combine(weights=False)
+    torch.cuda.synchronize()
+    ref = oracle.combine(ys, w.topk_idx, L, None)
+    assert np.array_equal(u16(run.out), ref)
+
+
+def test_backward_rejects_half_given_grad_w():
+    w, run, L, ys = prep("tiny")
+    g = torch.zeros((w.T, w.H), dtype=torch.int16, device="cuda")
+    rows = rows_to_dev(run.cap, w.H, [np.zeros((0, w.H), np.uint16)] * w.R)
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_combine_backward(run.cfg, run.h, run.idx, g, run.wts, rows, rows, None, run.cap)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
