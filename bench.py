@@ -374,7 +374,34 @@ def main():
         assert int(h.error_flag.item()) == 0
         del shared, gout, grows, gwt
 
+        # decode-style steps: the one-call layout + dispatch, and the cached-
+        # handle step (gating unchanged: dispatch + combine, no layout)
+        def step_time(fns):
+            for _ in range(3):
+                for fn in fns:
+                    assert fn() == 0
+            torch.cuda.synchronize()
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = max(K, 20)
+            a.record(stream)
+            for _ in range(n):
+                for fn in fns:
+                    assert fn() == 0
+            b_.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b_) * 1e3 / n
+
+        ld = lambda: L.ep_layout_dispatch(pc, idx.data_ptr(), ph, ws.data_ptr(), x.data_ptr(), rx, rs,
+                                          cap, sp)
+        cd = lambda: L.ep_dispatch(pc, ph, idx.data_ptr(), x.data_ptr(), rx, rs, cap, sp)
+        cc = lambda: L.ep_combine(pc, ph, idx.data_ptr(), ry, wts.data_ptr(), out.data_ptr(), cap, sp)
+        extras["layout_dispatch_us"] = round(step_time([ld]), 2)
+        extras["fused_step_us"] = round(step_time([ld, cc]), 2)
+        extras["cached_handle_step_us"] = round(step_time([cd, cc]), 2)
+        assert int(h.error_flag.item()) == 0
+
     graph_us = None
+    fused_graph_us = None
     if args.graph:
         # one step (layout + dispatch + combine) captured once, replayed K times
         gs = torch.cuda.Stream()
@@ -397,6 +424,25 @@ def main():
         gb.record()
         torch.cuda.synchronize()
         graph_us = ga.elapsed_time(gb) * 1e3 / K
+        assert int(h.error_flag.item()) == 0
+        # the fused step (ep_layout_dispatch + ep_combine) as a graph
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g2, stream=gs):
+                assert L.ep_layout_dispatch(pc, idx.data_ptr(), ph, ws.data_ptr(), x.data_ptr(), rx,
+                                            rs, cap, gsp) == 0
+                assert L.ep_combine(pc, ph, idx.data_ptr(), ry, wts.data_ptr(), out.data_ptr(), cap,
+                                    gsp) == 0
+        stream.wait_stream(gs)
+        for _ in range(args.warmup):
+            g2.replay()
+        torch.cuda.synchronize()
+        ga.record()
+        for _ in range(K):
+            g2.replay()
+        gb.record()
+        torch.cuda.synchronize()
+        fused_graph_us = ga.elapsed_time(gb) * 1e3 / K
         assert int(h.error_flag.item()) == 0
 
     res = {
@@ -432,6 +478,7 @@ def main():
         "write_ceiling_GBps": round(write_gbps, 1),
         "bytes_per_step": step_bytes,
         "graph_step_us": None if graph_us is None else round(graph_us, 2),
+        "fused_graph_step_us": None if fused_graph_us is None else round(fused_graph_us, 2),
         "extras": extras,
         "cpu_baseline": None,
     }

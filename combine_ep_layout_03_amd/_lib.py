@@ -22,8 +22,8 @@ EP_MAX_RANKS, EP_MAX_TOPK, EP_MAX_EXPERTS, EP_MAX_HIDDEN = 64, 32, 2048, 65536
 
 # Every symbol include/ep.h declares.
 EXPORTS = ("ep_abi_version", "ep_status_string", "ep_recv_capacity_rows",
-           "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine",
-           "ep_combine_shared", "ep_combine_backward", "ep_unpermute")
+           "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_layout_dispatch",
+           "ep_combine", "ep_combine_shared", "ep_combine_backward", "ep_unpermute")
 
 
 class EpError(RuntimeError):
@@ -74,6 +74,9 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.ep_layout.argtypes = [cfgp, vp, hp, vp, vp]
     L.ep_dispatch.restype = ctypes.c_int32
     L.ep_dispatch.argtypes = [cfgp, hp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, vp]
+    L.ep_layout_dispatch.restype = ctypes.c_int32
+    L.ep_layout_dispatch.argtypes = [cfgp, vp, hp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                     i64, vp]
     L.ep_combine.restype = ctypes.c_int32
     L.ep_combine.argtypes = [cfgp, hp, vp, ctypes.POINTER(vp), vp, vp, i64, vp]
     L.ep_combine_shared.restype = ctypes.c_int32
@@ -168,6 +171,15 @@ def ep_dispatch(cfg, handle, topk_idx, x, recv_x, recv_scales, capacity_rows, st
     _check(load().ep_dispatch(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)), _ptr(topk_idx),
                               _ptr(x), _ptrs(recv_x), rs, int(capacity_rows), _stream(stream)),
            "ep_dispatch")
+
+
+def ep_layout_dispatch(cfg, topk_idx, handle, workspace, x, recv_x, recv_scales, capacity_rows,
+                       stream=None) -> None:
+    rs = None if recv_scales is None else _ptrs(recv_scales)
+    _check(load().ep_layout_dispatch(ctypes.byref(_cfg(cfg)), _ptr(topk_idx),
+                                     ctypes.byref(_handle(handle)), _ptr(workspace), _ptr(x),
+                                     _ptrs(recv_x), rs, int(capacity_rows), _stream(stream)),
+           "ep_layout_dispatch")
 
 
 def ep_combine(cfg, handle, topk_idx, recv_y, topk_weights, out, capacity_rows, stream=None) -> None:

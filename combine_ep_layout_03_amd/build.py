@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libep.so")
 
-SOURCES = ["ep_api.cpp", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip"]
+SOURCES = ["ep_api.cpp", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_fused.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
@@ -48,7 +48,8 @@ def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    deps = sources() + [os.path.join(CSRC, "ep_internal.h"), os.path.join(INCLUDE, "ep.h")]
+    deps = sources() + [os.path.join(CSRC, "ep_internal.h"), os.path.join(CSRC, "ep_device.h"),
+                        os.path.join(INCLUDE, "ep.h")]
     return any(os.path.getmtime(d) > t for d in deps)
 
 

@@ -112,6 +112,39 @@ ep_status ep_dispatch(const ep_config *cfg, const ep_layout_t *h, const int32_t 
   return from_hip(ep::launch_dispatch(*cfg, *h, topk_idx, x, rx, rs, capacity_rows, stream));
 }
 
+ep_status ep_layout_dispatch(const ep_config *cfg, const int32_t *topk_idx, const ep_layout_t *h,
+                             void *workspace, const void *x, void *const *recv_x,
+                             float *const *recv_scales, int64_t capacity_rows,
+                             hipStream_t stream) {
+  if (!config_ok(cfg) || !handle_ok(h) || !topk_idx || !workspace) return EP_ERR_INVALID_ARG;
+  ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
+  if (st != EP_OK) return st;
+  if (!x || !recv_x) return EP_ERR_INVALID_ARG;
+  const bool fp8 = cfg->dispatch_dtype == EP_DTYPE_FP8_E4M3;
+  if (fp8 && !recv_scales) return EP_ERR_INVALID_ARG;
+  ep::RankPtrs rx{};
+  ep::ScalePtrs rs{};
+  for (int r = 0; r < cfg->num_ranks; ++r) {
+    if (!recv_x[r]) return EP_ERR_INVALID_ARG;
+    rx.p[r] = recv_x[r];
+    if (fp8) {
+      if (!recv_scales[r]) return EP_ERR_INVALID_ARG;
+      rs.p[r] = recv_scales[r];
+    }
+  }
+  if (ep::fused_layout_dispatch_ok(*cfg)) {
+    trace("layout_dispatch (one launch)", cfg, 0);
+    return from_hip(
+        ep::launch_layout_dispatch_small(*cfg, topk_idx, *h, x, rx, rs, capacity_rows, stream));
+  }
+  const ep::LayoutPlan plan =
+      ep::plan_layout((int64_t)cfg->num_tokens * cfg->num_topk, cfg->num_experts);
+  hipError_t e = ep::launch_layout(*cfg, plan, topk_idx, *h, workspace, stream);
+  if (e != hipSuccess) return EP_ERR_HIP;
+  trace("layout_dispatch (layout, then dispatch)", cfg, ep::row_grid(*cfg, cfg->num_tokens));
+  return from_hip(ep::launch_dispatch(*cfg, *h, topk_idx, x, rx, rs, capacity_rows, stream));
+}
+
 ep_status ep_combine(const ep_config *cfg, const ep_layout_t *h, const int32_t *topk_idx,
                      const void *const *recv_y, const float *topk_weights, void *out,
                      int64_t capacity_rows, hipStream_t stream) {

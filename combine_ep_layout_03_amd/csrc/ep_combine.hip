@@ -22,28 +22,17 @@
 // into the loads.  (Measured on MI355X at T=8192, H=7168, k=8: one-wave
 // workgroups and two chunks per lane beat four-wave workgroups, one chunk and
 // four chunks per lane; plain stores are slower than non-temporal ones.)
+#include "ep_device.h"
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
 
+using namespace dev;
+
 constexpr int kThreads = kRowWaves * kWave;
 constexpr int kJB = 8;                 // rows whose loads are issued together
 constexpr int kSegChunks = 2 * kWave;  // 16-byte chunks per work unit
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ inline uint64_t readlane64(uint64_t v, int lane) {
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// binary32 -> bf16 bits, nearest with ties to even; NaN stays a quiet NaN.
-__device__ inline uint32_t bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 // acc[0..7] += w * (8 bf16 of v), element by element, one fma each.
 __device__ inline void fma8(float *acc, float w, u32x4 v) {

@@ -1,0 +1,106 @@
+// ep_device.h -- device helpers shared by the HIP kernels of libep (codecs,
+// wave primitives).  Kernel-side only.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "ep_internal.h"
+
+namespace ep {
+namespace dev {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ inline int32_t wave_inclusive_scan(int32_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int32_t n = __shfl_up(v, d, kWave);
+    if (lane >= d) v += n;
+  }
+  return v;
+}
+
+__device__ inline int32_t wave_sum(int32_t v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// OCP E4M3 ("fn") of a binary32 value, nearest-even, saturating at 448.
+// Normal results: round the binary32 significand to 3 bits on the bit
+// pattern and rebias the exponent (127 -> 7).  Below 2^-6 the E4M3 spacing is
+// 2^-9, so the code is rint(|v| * 2^9) (the scaling is exact).
+__device__ inline uint32_t e4m3_code(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x43E00000u)  // |v| >= 448 (NaN is never produced here)
+    return sign | (a > 0x7F800000u ? 0x7Fu : 0x7Eu);
+  if (a < 0x3C800000u)   // |v| < 2^-6
+    return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;  // exp8 | mant3, rounded
+  const uint32_t code = r - (120u << 3);
+  return sign | (code < 0x7Eu ? code : 0x7Eu);
+}
+
+// max over the low 15 bits (|x| of bf16, monotone for non-NaN) of 8 bf16.
+__device__ inline uint32_t bf16_absbits_max(u32x4 v, uint32_t m) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = v[i] & 0x7FFFu, hi = (v[i] >> 16) & 0x7FFFu;
+    m = lo > m ? lo : m;
+    m = hi > m ? hi : m;
+  }
+  return m;
+}
+
+// 4 bf16 pairs -> 8 E4M3 codes of (x / s) in 2 dwords, channel order kept.
+__device__ inline void quant8(u32x4 v, float s, bool zero, uint32_t &w0, uint32_t &w1) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16);
+    const float hi = __uint_as_float(v[i] & 0xFFFF0000u);
+    c[2 * i] = zero ? 0u : e4m3_code(lo / s);
+    c[2 * i + 1] = zero ? 0u : e4m3_code(hi / s);
+  }
+  w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+}
+
+// One lane's share of a 128-channel block (16 channels as two 16-byte bf16
+// vectors) -> 16 E4M3 codes and the block scale.  The 8 lanes of a block are
+// the aligned groups of 8 lanes; lanes outside the row pass zeros as whole
+// groups.  s = a/448 (correctly rounded), codes of the correctly rounded x/s.
+__device__ inline u32x4 quant_block16(u32x4 v0, u32x4 v1, float &s_out) {
+  uint32_t m = bf16_absbits_max(v1, bf16_absbits_max(v0, 0u));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 4, kWave));
+  const bool zero = (m == 0u);
+  const float s = zero ? 0.0f : __uint_as_float(m << 16) / 448.0f;
+  uint32_t q0, q1, q2, q3;
+  quant8(v0, s, zero, q0, q1);
+  quant8(v1, s, zero, q2, q3);
+  s_out = s;
+  return u32x4{q0, q1, q2, q3};
+}
+
+// binary32 -> bf16 bits, nearest with ties to even; NaN stays a quiet NaN.
+__device__ inline uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+}  // namespace dev
+}  // namespace ep

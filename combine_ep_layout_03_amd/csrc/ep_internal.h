@@ -40,6 +40,7 @@ constexpr int kRowWaves = 1;     // wavefronts per dispatch / combine workgroup
 constexpr int kSmallWaves = 16;  // wavefronts of the single-workgroup layout
 constexpr int64_t kSmallMaxPairs = 8192;    // T*k limit of the single-launch layout
 constexpr int kSmallMaxExperts = 384;       // E limit of the single-launch layout (LDS <= 64 KB)
+constexpr int64_t kFusedMaxPairs = 2048;    // T*k limit of the one-launch layout + dispatch
 
 LayoutPlan plan_layout(int64_t P, int E);
 
@@ -60,6 +61,11 @@ hipError_t launch_combine_backward(const ep_config &c, const ep_layout_t &h,
                                    const int32_t *topk_idx, const void *grad_out, const float *w,
                                    const RankCPtrs &ry, const RankPtrs &rg, float *grad_w,
                                    int64_t capacity_rows, hipStream_t s);
+
+bool fused_layout_dispatch_ok(const ep_config &c);
+hipError_t launch_layout_dispatch_small(const ep_config &c, const int32_t *topk_idx,
+                                        const ep_layout_t &h, const void *x, const RankPtrs &rx,
+                                        const ScalePtrs &rs, int64_t capacity_rows, hipStream_t s);
 
 hipError_t launch_unpermute(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
                             const RankCPtrs &ry, void *out, int64_t capacity_rows, hipStream_t s);

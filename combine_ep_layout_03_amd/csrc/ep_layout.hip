@@ -28,6 +28,7 @@
 // totals and its own chunks' prefixes before walking.  (Measured at T*k =
 // 65536: making every workgroup of one launch count all pairs itself costs
 // more in LDS atomics than the second launch does.)
+#include "ep_device.h"
 #include "ep_internal.h"
 
 namespace ep {
@@ -71,7 +72,8 @@ namespace {
 
 constexpr int kThreads = kLayoutWaves * kWave;
 
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+using dev::i32x4;
+using dev::wave_inclusive_scan;
 
 // Chunk histograms: wave c counts the pairs [c*S, c*S+S) in LDS and writes
 // column c of the expert-major table hist[E+1][C] (row E counts indices
@@ -117,15 +119,6 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(const int32_t *_
   __syncthreads();
   if (c < C)
     for (int e = lane; e < E1; e += kWave) hist[(int64_t)e * C + c] = h[e];
-}
-
-__device__ inline int32_t wave_inclusive_scan(int32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int32_t n = __shfl_up(v, d, kWave);
-    if (lane >= d) v += n;
-  }
-  return v;
 }
 
 // Exclusive scan of a[0..n) in place, a[n] = total.  All NT threads of the

@@ -164,6 +164,21 @@ ep_status ep_dispatch(const ep_config *cfg /*(host)*/, const ep_layout_t *h /*(h
                       void *const *recv_x /*(host)[R]*/, float *const *recv_scales /*(host)[R]*/,
                       int64_t capacity_rows, hipStream_t stream);
 
+/* Layout and dispatch in one call, for small batches (decode): the same
+ * handle and the same receive bytes as ep_layout followed by ep_dispatch
+ * ([Perplexity blog] "CUDA-graf": a decode step is bound by launch overhead).
+ * With T*k <= 2048 this is ONE kernel launch: every workgroup reads the
+ * whole index array and derives the offsets itself, so none waits for
+ * another.  Larger inputs run ep_layout's and ep_dispatch's kernels, so
+ * `workspace` must hold ep_layout_workspace_bytes(cfg) bytes either way.
+ * Arguments and errors as for ep_layout and ep_dispatch; an index outside
+ * [0,E) sets EP_DEVERR_INDEX and nothing is dispatched. */
+ep_status ep_layout_dispatch(const ep_config *cfg /*(host)*/, const int32_t *topk_idx,
+                             const ep_layout_t *h /*(host)*/, void *workspace, const void *x,
+                             void *const *recv_x /*(host)[R]*/,
+                             float *const *recv_scales /*(host)[R]*/, int64_t capacity_rows,
+                             hipStream_t stream);
+
 /* Combine ([Perplexity blog] "Sérfræðinga-samsíðun": the routed results are
  * weighted and summed; [DeepEP overview] "Pola penggunaan ...": combine
  * reduces expert outputs back to the source).  For every token t and channel
