@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.oracle_combine_shared.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_combine_backward.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_silu_mul_row.argtypes = [i32, vp, vp]
+        L.oracle_silu_mul_quant_row.argtypes = [i32, vp, vp, vp]
+        L.oracle_quantize_f32_row.argtypes = [i32, vp, vp, vp]
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
@@ -276,6 +279,39 @@ def combine_backward(grad_out: np.ndarray, topk_idx: np.ndarray, L: Layout, weig
                                   _ptr_array(_rows_or_empty(gr, H)),
                                   None if gw is None else _p(gw))
     return gr, gw
+
+
+def silu_mul(rows: np.ndarray) -> np.ndarray:
+    """a = RN32(silu(gate) * up) per row of 2I bf16 values -> [n, I] float32."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+    n, I2 = rows.shape
+    a = np.empty((n, I2 // 2), np.float32)
+    for i in range(n):
+        lib().oracle_silu_mul_row(I2 // 2, _p(rows[i]), _p(a[i]))
+    return a
+
+
+def silu_mul_quant(rows: np.ndarray):
+    """SiLU-and-multiply then per-128 FP8 quantization, per row of 2I bf16
+    values -> (q [n, I] uint8, s [n, I/128] float32)."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+    n, I2 = rows.shape
+    I = I2 // 2
+    q = np.empty((n, I), np.uint8)
+    s = np.empty((n, I // 128), np.float32)
+    for i in range(n):
+        lib().oracle_silu_mul_quant_row(I, _p(rows[i]), _p(q[i]), _p(s[i]))
+    return q, s
+
+
+def quantize_f32_rows(a: np.ndarray):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    n, I = a.shape
+    q = np.empty((n, I), np.uint8)
+    s = np.empty((n, I // 128), np.float32)
+    for i in range(n):
+        lib().oracle_quantize_f32_row(I, _p(a[i]), _p(q[i]), _p(s[i]))
+    return q, s
 
 
 def dequant_identity_expert(recv_q, recv_s):

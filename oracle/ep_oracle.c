@@ -366,3 +366,49 @@ void oracle_combine_backward(int T, int H, int k, int E, int R, const int32_t *i
         }
     }
 }
+
+/* ------------------------------------------------- expert-side activation */
+
+void oracle_quantize_f32_row(int n, const float *a, uint8_t *q, float *s)
+{
+    /* the same steps as oracle_quantize_row, on binary32 activations */
+    for (int b = 0; b < n / 128; ++b) {
+        const float *ab = a + b * 128;
+        float amax = 0.0f;
+        for (int h = 0; h < 128; ++h) {
+            float v = fabsf(ab[h]);
+            if (v > amax)
+                amax = v;
+        }
+        if (amax == 0.0f) {
+            s[b] = 0.0f;
+            for (int h = 0; h < 128; ++h)
+                q[b * 128 + h] = 0x00;
+            continue;
+        }
+        float sb = amax / 448.0f;
+        s[b] = sb;
+        for (int h = 0; h < 128; ++h)
+            q[b * 128 + h] = oracle_e4m3_encode(ab[h] / sb);
+    }
+}
+
+void oracle_silu_mul_row(int I, const uint16_t *row, float *a)
+{
+    for (int h = 0; h < I; ++h) {
+        double g = (double)oracle_bf16_to_f32(row[h]);
+        double u = (double)oracle_bf16_to_f32(row[I + h]);
+        double silu = g / (1.0 + exp(-g));
+        a[h] = (float)(silu * u);
+    }
+}
+
+void oracle_silu_mul_quant_row(int I, const uint16_t *row, uint8_t *q, float *s)
+{
+    float *a = (float *)malloc((size_t)I * sizeof(float));
+    if (!a)
+        return;
+    oracle_silu_mul_row(I, row, a);
+    oracle_quantize_f32_row(I, a, q, s);
+    free(a);
+}

@@ -99,6 +99,18 @@ void oracle_combine_backward(int T, int H, int k, int E, int R, const int32_t *i
                              const uint16_t *const *recv_y, uint16_t *const *grad_recv,
                              float *grad_w);
 
+/* Expert activation with block re-quantization ([Perplexity blog],
+ * "Magntölun": the SiLU kernel splits the hidden dimension into blocks and
+ * quantizes per 128 elements, with scales computed on the fly).  For one
+ * row of 2I bf16 values (gate = row[0:I], up = row[I:2I]):
+ *   a[h] = RN32( silu(g) * u ),  silu(v) = v / (1 + e^-v), all in binary64;
+ * then per 128-element block of a exactly as oracle_quantize_row:
+ *   s = RN32(amax/448), q = E4M3(RN32(a/s)); an all-zero block gives s = 0,
+ *   q = 0x00.  oracle_silu_mul_row stops after a. */
+void oracle_silu_mul_row(int I, const uint16_t *row, float *a);
+void oracle_silu_mul_quant_row(int I, const uint16_t *row, uint8_t *q, float *s);
+void oracle_quantize_f32_row(int n, const float *a, uint8_t *q, float *s);
+
 /* Codecs. */
 uint8_t  oracle_e4m3_encode(float v);
 float    oracle_e4m3_decode(uint8_t c);
