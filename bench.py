@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 CAL_BYTES = 1 << 30  # size of the calibration kernels (elementwise copy, fill)
+EXPERT_I = 2048      # expert intermediate size for the SiLU stage (DeepSeek-V3's)
 METRIC = "dispatch+combine µs and achieved HBM GB/s at 8K tok, h7168, top-8, 1 GPU"
 
 
@@ -55,6 +56,8 @@ def extra_bytes(T, H, k):
         "combine_shared": 2 * H * P + 2 * H * T + 2 * H * T + 12 * P,
         # read grad_out, read y, write the gradient rows, read w/idx/slot, write grad_w
         "combine_backward": 2 * H * T + 2 * H * P + 2 * H * P + 12 * P + 4 * P,
+        # per received row: read 2I bf16, write I codes and I/128 scales (I = 2048)
+        "silu_mul_quant": P * (4 * EXPERT_I + EXPERT_I + 4 * (EXPERT_I // 128)),
     }
 
 
@@ -350,7 +353,22 @@ def main():
         gwt = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
         rgp = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in grows])
         xb = extra_bytes(w.T, w.H, w.k)
+        # expert GEMM-1 outputs (gate | up, 2*EXPERT_I bf16) in the receive
+        # layout: capacity-sized buffers, seeded rows in the valid part
+        act, aq, asc = [], [], []
+        for r in range(w.R):
+            a = torch.zeros((cap, 2 * EXPERT_I), dtype=torch.int16, device=dev)
+            if rank_counts[r]:
+                a[:rank_counts[r]] = torch.randn((rank_counts[r], 2 * EXPERT_I), generator=gen,
+                                                 device=dev).to(torch.bfloat16).view(torch.int16)
+            act.append(a)
+            aq.append(torch.empty((cap, EXPERT_I), dtype=torch.uint8, device=dev))
+            asc.append(torch.empty((cap, EXPERT_I // 128), dtype=torch.float32, device=dev))
+        pa = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in act])
+        pq = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in aq])
+        ps = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in asc])
         calls = {
+            "silu_mul_quant": lambda: L.ep_silu_mul_quant(pc, ph, EXPERT_I, pa, pq, ps, cap, sp),
             "combine_shared": lambda: L.ep_combine_shared(pc, ph, idx.data_ptr(), ry, wts.data_ptr(),
                                                           shared.data_ptr(), out.data_ptr(), cap, sp),
             "combine_backward": lambda: L.ep_combine_backward(pc, ph, idx.data_ptr(), gout.data_ptr(),
@@ -372,7 +390,7 @@ def main():
             extras[name] = {"us": round(us, 2), "algorithmic_bytes": xb[name],
                             "GBps": round(xb[name] / (us * 1e-6) / 1e9, 1)}
         assert int(h.error_flag.item()) == 0
-        del shared, gout, grows, gwt
+        del shared, gout, grows, gwt, act, aq, asc
 
         # decode-style steps: the one-call layout + dispatch, and the cached-
         # handle step (gating unchanged: dispatch + combine, no layout)

@@ -23,7 +23,8 @@ EP_MAX_RANKS, EP_MAX_TOPK, EP_MAX_EXPERTS, EP_MAX_HIDDEN = 64, 32, 2048, 65536
 # Every symbol include/ep.h declares.
 EXPORTS = ("ep_abi_version", "ep_status_string", "ep_recv_capacity_rows",
            "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_layout_dispatch",
-           "ep_combine", "ep_combine_shared", "ep_combine_backward", "ep_unpermute")
+           "ep_combine", "ep_combine_shared", "ep_combine_backward", "ep_silu_mul_quant",
+           "ep_unpermute")
 
 
 class EpError(RuntimeError):
@@ -84,6 +85,9 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.ep_combine_backward.restype = ctypes.c_int32
     L.ep_combine_backward.argtypes = [cfgp, hp, vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                       vp, i64, vp]
+    L.ep_silu_mul_quant.restype = ctypes.c_int32
+    L.ep_silu_mul_quant.argtypes = [cfgp, hp, ctypes.c_int32, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                    ctypes.POINTER(vp), i64, vp]
     L.ep_unpermute.restype = ctypes.c_int32
     L.ep_unpermute.argtypes = [cfgp, hp, vp, ctypes.POINTER(vp), vp, i64, vp]
     return L
@@ -204,6 +208,14 @@ def ep_combine_backward(cfg, handle, topk_idx, grad_out, topk_weights, recv_y, g
                                       _ptrs(grad_recv), _ptr(grad_weights), int(capacity_rows),
                                       _stream(stream)),
            "ep_combine_backward")
+
+
+def ep_silu_mul_quant(cfg, handle, intermediate, act_in, q_out, scales_out, capacity_rows,
+                      stream=None) -> None:
+    _check(load().ep_silu_mul_quant(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)),
+                                    int(intermediate), _ptrs(act_in), _ptrs(q_out),
+                                    _ptrs(scales_out), int(capacity_rows), _stream(stream)),
+           "ep_silu_mul_quant")
 
 
 def ep_unpermute(cfg, handle, topk_idx, recv_y, out, capacity_rows, stream=None) -> None:

@@ -201,6 +201,28 @@ ep_status ep_combine_backward(const ep_config *cfg, const ep_layout_t *h, const 
                                               grad_weights, capacity_rows, stream));
 }
 
+ep_status ep_silu_mul_quant(const ep_config *cfg, const ep_layout_t *h, int32_t intermediate,
+                            const void *const *act_in, void *const *q_out,
+                            float *const *scales_out, int64_t capacity_rows, hipStream_t stream) {
+  if (!config_ok(cfg) || !handle_ok(h)) return EP_ERR_INVALID_ARG;
+  if (intermediate < 128 || intermediate % 128 != 0 || intermediate > EP_MAX_HIDDEN)
+    return EP_ERR_INVALID_ARG;
+  if (capacity_rows < (int64_t)cfg->num_tokens * cfg->num_topk) return EP_ERR_CAPACITY;
+  if (!act_in || !q_out || !scales_out) return EP_ERR_INVALID_ARG;
+  ep::RankCPtrs in{};
+  ep::RankPtrs q{};
+  ep::ScalePtrs s{};
+  for (int r = 0; r < cfg->num_ranks; ++r) {
+    if (!act_in[r] || !q_out[r] || !scales_out[r]) return EP_ERR_INVALID_ARG;
+    in.p[r] = act_in[r];
+    q.p[r] = q_out[r];
+    s.p[r] = scales_out[r];
+  }
+  trace("silu_mul_quant", cfg, 0);
+  return from_hip(ep::launch_silu_mul_quant(*cfg, *h, intermediate, in, q, s, capacity_rows,
+                                            stream));
+}
+
 ep_status ep_unpermute(const ep_config *cfg, const ep_layout_t *h, const int32_t *topk_idx,
                        const void *const *recv_y, void *out, int64_t capacity_rows,
                        hipStream_t stream) {

@@ -95,6 +95,32 @@ __device__ inline u32x4 quant_block16(u32x4 v0, u32x4 v1, float &s_out) {
   return u32x4{q0, q1, q2, q3};
 }
 
+// The same block quantization on 16 binary32 values per lane (8 lanes per
+// 128-element block): amax on |a| bit patterns, s = a/448, codes of a/s.
+__device__ inline u32x4 quant_block16_f32(const float *a, float &s_out) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t b = __float_as_uint(a[i]) & 0x7FFFFFFFu;
+    m = b > m ? b : m;
+  }
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 4, kWave));
+  const bool zero = (m == 0u);
+  const float s = zero ? 0.0f : __uint_as_float(m) / 448.0f;
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = zero ? 0u : e4m3_code(a[4 * i + j] / s);
+    w[i] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  }
+  s_out = s;
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
 // binary32 -> bf16 bits, nearest with ties to even; NaN stays a quiet NaN.
 __device__ inline uint32_t bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);

@@ -1,0 +1,95 @@
+// ep_expert.hip -- expert-side activation on the received rows: SiLU-and-
+// multiply followed by per-128-channel FP8 re-quantization.
+//
+// Pages: [Perplexity blog] "Lower latency and higher throughput with
+// multi-node DeepSeek deployment", "Magntölun": the SiLU kernel quantizes its
+// output per 128-element block with scales computed on the fly, and, under
+// graphs, reads the per-expert token counts on the device and splits the
+// work dynamically instead of sizing it from the upper-bound buffers.
+//
+// Design.  The input rows are the expert GEMM's outputs in the receive
+// layout (R rank buffers, rows in slot order); the number of valid rows is
+// T*k in total, split over the ranks by the handle's rank_offsets, which the
+// kernel reads on the device (a binary search per work unit), so the launch
+// needs no host copy of the counts and can be captured in a graph.  A unit is
+// (slot, segment of 8 blocks of 128 channels); a lane holds 16 channels of
+// gate and up, computes a = g * rcp(1 + e^-g) * u in binary32 (the device
+// expf and the 1-ulp hardware reciprocal: the activation is specified to a
+// tolerance against a binary64 reference, and the correctly rounded divide
+// made this ALU-bound) and then the block amax / scale / codes exactly as
+// dispatch does (a correctly rounded a/s).
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+using namespace dev;
+
+constexpr int kSegBlocks = 8;
+
+__global__ __launch_bounds__(kWave) void silu_mul_quant_kernel(
+    const int32_t *__restrict__ rank_offsets, const int32_t *__restrict__ err, int64_t P,
+    int32_t R, int32_t I, int64_t cap, RankCPtrs in, RankPtrs q_out, ScalePtrs s_out) {
+  if (*err != 0) return;
+  const int lane = threadIdx.x;
+  const int nb = I / 128;
+  const int nseg = (nb + kSegBlocks - 1) / kSegBlocks;
+  const int64_t units = P * nseg;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t slot = u / nseg;
+    const int seg = (int)(u % nseg);
+    // rank r with rank_offsets[r] <= slot < rank_offsets[r+1] (uniform)
+    int lo = 0, hi = R;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (rank_offsets[mid] <= slot) lo = mid;
+      else hi = mid;
+    }
+    const int64_t row = slot - rank_offsets[lo];
+    if (row < 0 || row >= cap) continue;  // cannot happen for a valid handle
+    const int blk = seg * kSegBlocks + lane / 8;
+    const bool valid = blk < nb;
+    const int ch = blk * 128 + (lane % 8) * 16;
+    const uint16_t *src = static_cast<const uint16_t *>(in.p[lo]) + row * (int64_t)(2 * I);
+    u32x4 g0 = {0u, 0u, 0u, 0u}, g1 = g0, u0 = g0, u1 = g0;
+    if (valid) {
+      g0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + ch));
+      g1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + ch + 8));
+      u0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + I + ch));
+      u1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + I + ch + 8));
+    }
+    float a[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4 gv = i < 4 ? g0 : g1, uv = i < 4 ? u0 : u1;
+      const uint32_t gw = gv[i % 4], uw = uv[i % 4];
+      const float ga = __uint_as_float(gw << 16), gb = __uint_as_float(gw & 0xFFFF0000u);
+      const float ua = __uint_as_float(uw << 16), ub = __uint_as_float(uw & 0xFFFF0000u);
+      a[2 * i] = ga * __builtin_amdgcn_rcpf(1.0f + expf(-ga)) * ua;
+      a[2 * i + 1] = gb * __builtin_amdgcn_rcpf(1.0f + expf(-gb)) * ub;
+    }
+    float s;
+    const u32x4 q = quant_block16_f32(a, s);
+    if (valid) {
+      uint8_t *qd = static_cast<uint8_t *>(q_out.p[lo]) + row * (int64_t)I;
+      __builtin_nontemporal_store(q, reinterpret_cast<u32x4 *>(qd + ch));
+      if ((lane % 8) == 0) s_out.p[lo][row * nb + blk] = s;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_silu_mul_quant(const ep_config &c, const ep_layout_t &h, int32_t I,
+                                 const RankCPtrs &in, const RankPtrs &q, const ScalePtrs &s,
+                                 int64_t capacity_rows, hipStream_t st) {
+  const int64_t P = (int64_t)c.num_tokens * c.num_topk;
+  const int64_t nseg = (I / 128 + kSegBlocks - 1) / kSegBlocks;
+  const int grid = row_grid(c, P * nseg);
+  hipLaunchKernelGGL(silu_mul_quant_kernel, dim3(grid), dim3(kWave), 0, st, h.rank_offsets,
+                     h.error_flag, P, c.num_ranks, I, capacity_rows, in, q, s);
+  return hipGetLastError();
+}
+
+}  // namespace ep

@@ -62,6 +62,10 @@ hipError_t launch_combine_backward(const ep_config &c, const ep_layout_t &h,
                                    const RankCPtrs &ry, const RankPtrs &rg, float *grad_w,
                                    int64_t capacity_rows, hipStream_t s);
 
+hipError_t launch_silu_mul_quant(const ep_config &c, const ep_layout_t &h, int32_t I,
+                                 const RankCPtrs &in, const RankPtrs &q, const ScalePtrs &s,
+                                 int64_t capacity_rows, hipStream_t st);
+
 bool fused_layout_dispatch_ok(const ep_config &c);
 hipError_t launch_layout_dispatch_small(const ep_config &c, const int32_t *topk_idx,
                                         const ep_layout_t &h, const void *x, const RankPtrs &rx,

@@ -222,6 +222,25 @@ ep_status ep_combine_backward(const ep_config *cfg /*(host)*/, const ep_layout_t
                               void *const *grad_recv /*(host)[R]*/, float *grad_weights,
                               int64_t capacity_rows, hipStream_t stream);
 
+/* Expert activation on the received rows ([Perplexity blog] "Magntölun":
+ * SiLU with per-128-element block quantization, scales on the fly, work
+ * split from device-side token counts under graphs).  For every received row
+ * (the T*k slots, mapped to rank r and row with the handle's rank_offsets on
+ * the device): gate = act_in row [0, I), up = [I, 2I) (bf16);
+ *   a = g * rcp(1 + expf(-g)) * u in fp32 (the device library's expf and
+ *   the hardware reciprocal; a few fp32 ulps from the binary64 value), then
+ *   per 128-element block s = a_max/448 and q = E4M3(a/s) as in ep_dispatch.
+ * act_in: (host) R pointers to [capacity_rows, 2I] bf16; q_out: (host) R
+ * pointers to [capacity_rows, I] bytes; scales_out: (host) R pointers to
+ * [capacity_rows, I/128] fp32.  intermediate = I, a multiple of 128.  Rows
+ * past rank_counts[r] are not read or written.  Results match a binary64
+ * reference to E4M3 rounding (codes can differ where the fp32 activation
+ * sits on a rounding boundary). */
+ep_status ep_silu_mul_quant(const ep_config *cfg /*(host)*/, const ep_layout_t *h /*(host)*/,
+                            int32_t intermediate, const void *const *act_in /*(host)[R]*/,
+                            void *const *q_out /*(host)[R]*/, float *const *scales_out /*(host)[R]*/,
+                            int64_t capacity_rows, hipStream_t stream);
+
 /* Un-permute ([torchtitan PR]: the token unpermute after the experts) as a
  * standalone call for testing: out[p] (H bf16) := recv_y[r(p)] row row(p), so
  * out is [T*k, H] in (t, j) order.  Same arguments and errors as ep_combine. */

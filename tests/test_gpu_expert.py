@@ -1,0 +1,80 @@
+"""GPU parity of ep_silu_mul_quant (SiLU-and-multiply with per-128 FP8
+re-quantization on the received rows) against the oracle.
+
+The oracle's activation is binary64 rounded once to fp32; the kernel's is
+binary32 with the device expf, within a few fp32 ulps of it.  So the bar is:
+scales within a relative 1e-6; every code's dequantized value within the
+E4M3 half-ulp bound of the oracle's activation, max(2^-4 |a|, 2^-10 s), plus
+1e-6 of slack for that activation error; and (reported) almost every code
+identical.  Rows past rank_counts[r] must stay untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_layout_03_amd as ep
+import oracle
+from workloads import make_workload, bf16_from_f32
+
+from gpu_util import GpuRun, POISON, rows_to_dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ep.load()
+
+
+def check_silu(name, T, I, scale=1.5, seed=0):
+    w = make_workload(name, T=T)
+    run = GpuRun(w).layout()
+    L = oracle.layout(w.topk_idx, w.E, w.R)
+    rng = np.random.default_rng(seed)
+    act = bf16_from_f32((rng.standard_normal((w.P, 2 * I)) * scale).astype(np.float32))
+    act_r = [act[L.rank_offsets[r]:L.rank_offsets[r + 1]] for r in range(w.R)]
+    ins = rows_to_dev(run.cap, 2 * I, act_r)
+    qs = [torch.full((run.cap, I), POISON, dtype=torch.uint8, device="cuda") for _ in range(w.R)]
+    ss = [torch.full((run.cap, I // 128), float("nan"), dtype=torch.float32, device="cuda")
+          for _ in range(w.R)]
+    say(f"silu_mul_quant {name} T={w.T} rows={w.P} I={I}")
+    ep.ep_silu_mul_quant(run.cfg, run.h, I, ins, qs, ss, run.cap)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.silu_mul_quant(act)
+    a_ref = oracle.silu_mul(act).astype(np.float64)
+    same = total = 0
+    for r in range(w.R):
+        n = int(L.rank_counts[r])
+        lo = int(L.rank_offsets[r])
+        q = qs[r].cpu().numpy()
+        s = ss[r].cpu().numpy()
+        assert np.all(q[n:] == POISON) and np.all(np.isnan(s[n:]))
+        q, s = q[:n], s[:n]
+        qr, sr, ar = q_ref[lo:lo + n], s_ref[lo:lo + n], a_ref[lo:lo + n]
+        assert np.all(np.abs(s.astype(np.float64) - sr) <= 1e-6 * np.abs(sr))
+        assert np.array_equal(s == 0, sr == 0)
+        dec = oracle.e4m3_decode(q).astype(np.float64) * np.repeat(s.astype(np.float64), 128, axis=1)
+        sg = np.repeat(s.astype(np.float64), 128, axis=1)
+        bound = np.maximum(2.0 ** -4 * np.abs(ar), 2.0 ** -10 * sg) * (1 + 1e-5) + 1e-6 * (np.abs(ar) + sg)
+        assert np.all(np.abs(dec - ar) <= bound), f"rank {r}"
+        same += int(np.count_nonzero(q == qr))
+        total += q.size
+    say(f"  identical codes: {same}/{total} ({100.0 * same / max(total, 1):.5f} %)")
+    assert same >= 0.999 * total
+
+
+@pytest.mark.parametrize("name,T,I", [("decode", None, 2048), ("tiny", None, 256), ("ds16b", 512, 1408),
+                                      ("v3", 1024, 2048), ("v3_skew", 512, 2048)])
+def test_silu_mul_quant(name, T, I):
+    check_silu(name, T, I)
+
+
+def test_silu_mul_quant_wide_range():
+    # large |gate| (saturating sigmoid) and tiny values
+    check_silu("decode", 64, 1024, scale=12.0, seed=5)
+
+
+def test_silu_mul_quant_full_headline():
+    check_silu("v3", None, 2048)
