@@ -38,7 +38,11 @@ __device__ inline int32_t wave_sum(int32_t v) {
 // OCP E4M3 ("fn") of a binary32 value, nearest-even, saturating at 448.
 // Normal results: round the binary32 significand to 3 bits on the bit
 // pattern and rebias the exponent (127 -> 7).  Below 2^-6 the E4M3 spacing is
-// 2^-9, so the code is rint(|v| * 2^9) (the scaling is exact).
+// 2^-9, so the code is rint(|v| * 2^9) (the scaling is exact).  This is the
+// software statement of the conversion; the quantizers below use gfx950's
+// v_cvt_pk_fp8_f32, which gives the same byte for every binary32 value with
+// |v| <= 450 (all 2^31 + signs checked on MI355X); quotients x/s never leave
+// that range (|x/s| <= 448 * (1 + 2^-23)).
 __device__ inline uint32_t e4m3_code(float v) {
   const uint32_t u = __float_as_uint(v);
   const uint32_t sign = (u >> 24) & 0x80u;
@@ -63,18 +67,25 @@ __device__ inline uint32_t bf16_absbits_max(u32x4 v, uint32_t m) {
   return m;
 }
 
-// 4 bf16 pairs -> 8 E4M3 codes of (x / s) in 2 dwords, channel order kept.
+// Four binary32 values (each |v| <= 448 * (1 + 2^-23)) -> four E4M3 codes in
+// one dword, byte i = code of a_i (the hardware conversion, nearest-even).
+__device__ inline uint32_t e4m3_pack4(float a0, float a1, float a2, float a3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, w, true);
+  return (uint32_t)w;
+}
+
+// 4 bf16 pairs -> 8 E4M3 codes of (x / s) in 2 dwords, channel order kept;
+// zero (an all-zero block) gives 0x00 codes.
 __device__ inline void quant8(u32x4 v, float s, bool zero, uint32_t &w0, uint32_t &w1) {
-  uint32_t c[8];
+  float r[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float lo = __uint_as_float(v[i] << 16);
-    const float hi = __uint_as_float(v[i] & 0xFFFF0000u);
-    c[2 * i] = zero ? 0u : e4m3_code(lo / s);
-    c[2 * i + 1] = zero ? 0u : e4m3_code(hi / s);
+    r[2 * i] = __uint_as_float(v[i] << 16) / s;
+    r[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u) / s;
   }
-  w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-  w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  w0 = zero ? 0u : e4m3_pack4(r[0], r[1], r[2], r[3]);
+  w1 = zero ? 0u : e4m3_pack4(r[4], r[5], r[6], r[7]);
 }
 
 // One lane's share of a 128-channel block (16 channels as two 16-byte bf16
@@ -111,12 +122,8 @@ __device__ inline u32x4 quant_block16_f32(const float *a, float &s_out) {
   const float s = zero ? 0.0f : __uint_as_float(m) / 448.0f;
   uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t c[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = zero ? 0u : e4m3_code(a[4 * i + j] / s);
-    w[i] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-  }
+  for (int i = 0; i < 4; ++i)
+    w[i] = zero ? 0u : e4m3_pack4(a[4 * i] / s, a[4 * i + 1] / s, a[4 * i + 2] / s, a[4 * i + 3] / s);
   s_out = s;
   return u32x4{w[0], w[1], w[2], w[3]};
 }
