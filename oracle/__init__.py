@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_silu_mul_row.argtypes = [i32, vp, vp]
         L.oracle_silu_mul_quant_row.argtypes = [i32, vp, vp, vp]
         L.oracle_quantize_f32_row.argtypes = [i32, vp, vp, vp]
+        L.oracle_route.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.oracle_route.restype = i32
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
@@ -329,3 +331,33 @@ def dequant_identity_expert(recv_q, recv_s):
         prod = (d * sc).astype(np.float32)
         out.append(bf16_rne(prod))
     return out
+
+
+# ----------------------------------------------------------------- router
+GATES = {"softmax": 0, "sigmoid": 1}
+
+
+def route(logits: np.ndarray, k: int, gate: str = "sigmoid", n_groups: int = 1,
+          topk_groups: int = 1, group_topn: int = 2, renorm: bool = True, bias=None,
+          rep_offsets=None, rep_slots=None):
+    """Group-limited top-k router (oracle_route) -> (topk_idx [T,k] int32,
+    topk_weights [T,k] float32).  logits [T, El] float32; bias [El] float32 or
+    None; rep_offsets [El+1] / rep_slots int32 (redundant experts) or None."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, El = logits.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    ro = None if rep_offsets is None else np.ascontiguousarray(rep_offsets, dtype=np.int32)
+    rs = None if rep_slots is None else np.ascontiguousarray(rep_slots, dtype=np.int32)
+    if b is not None:
+        assert b.shape == (El,)
+    if ro is not None:
+        assert ro.shape == (El + 1,) and rs is not None and rs.size >= int(ro[-1])
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    rc = lib().oracle_route(T, El, k, GATES[gate], n_groups, topk_groups, group_topn, int(renorm),
+                            _p(logits), None if b is None else _p(b),
+                            None if ro is None else _p(ro), None if rs is None else _p(rs),
+                            _p(idx), _p(w))
+    if rc:
+        raise OracleError("router parameters rejected (code %d)" % rc)
+    return idx, w

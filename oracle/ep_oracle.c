@@ -412,3 +412,136 @@ void oracle_silu_mul_quant_row(int I, const uint16_t *row, uint8_t *q, float *s)
     oracle_quantize_f32_row(I, a, q, s);
     free(a);
 }
+
+/* ------------------------------------------------------------------ router */
+
+/* Expert (or group) a with score sa ranks above b with score sb: the larger
+ * score first, equal scores to the lower id.  Scores are compared as their
+ * binary32 bit patterns read as unsigned integers, which is numeric order for
+ * the non-negative scores a softmax or sigmoid gate gives (+0 < subnormals <
+ * normals < +inf) and still a total order when a NaN appears. */
+static int ranks_above(float sa, int a, float sb, int b)
+{
+    uint32_t ua, ub;
+    memcpy(&ua, &sa, sizeof ua);
+    memcpy(&ub, &sb, sizeof ub);
+    if (ua != ub)
+        return ua > ub;
+    return a < b;
+}
+
+int oracle_route(int T, int El, int k, int gate, int G, int TG, int group_topn, int renorm,
+                 const float *logits, const float *bias, const int32_t *rep_off,
+                 const int32_t *rep_slots, int32_t *idx, float *w)
+{
+    if (T < 1 || El < 1 || k < 1 || k > El || G < 1 || El % G != 0 || TG < 1 || TG > G ||
+        (gate != 0 && gate != 1) || (group_topn != 1 && group_topn != 2))
+        return 1;
+    const int gs = El / G;
+    if (k > TG * gs)
+        return 1;
+    const int n_top = group_topn < gs ? group_topn : gs;
+
+    float *z = malloc(sizeof(float) * (size_t)El);
+    float *s = malloc(sizeof(float) * (size_t)El);
+    double *ex = malloc(sizeof(double) * (size_t)El);
+    float *gsc = malloc(sizeof(float) * (size_t)G);
+    char *kept = malloc((size_t)G);
+    char *taken = malloc((size_t)El);
+    int *sel = malloc(sizeof(int) * (size_t)k);
+    float *ws = malloc(sizeof(float) * (size_t)k);
+
+    for (int t = 0; t < T; ++t) {
+        /* router input: logit plus the per-expert bias (one binary32 add) */
+        for (int e = 0; e < El; ++e)
+            z[e] = bias ? logits[(int64_t)t * El + e] + bias[e] : logits[(int64_t)t * El + e];
+
+        /* gate scores, evaluated in binary64 and rounded once to binary32 */
+        if (gate == 0) { /* softmax over the token's experts, max-subtracted */
+            float m = z[0];
+            for (int e = 1; e < El; ++e)
+                if (z[e] > m)
+                    m = z[e];
+            double sum = 0.0;
+            for (int e = 0; e < El; ++e) {
+                ex[e] = exp((double)z[e] - (double)m);
+                sum += ex[e];
+            }
+            for (int e = 0; e < El; ++e)
+                s[e] = (float)(ex[e] / sum);
+        } else { /* sigmoid */
+            for (int e = 0; e < El; ++e)
+                s[e] = (float)(1.0 / (1.0 + exp(-(double)z[e])));
+        }
+
+        /* group-limited routing: a group's score is its best score, or the
+         * binary32 sum of its two best; the TG best groups stay eligible.
+         * One group (G = 1) is plain top-k over every expert. */
+        for (int c = 0; c < G; ++c) {
+            int b1 = -1, b2 = -1;
+            for (int e = c * gs; e < (c + 1) * gs; ++e) {
+                if (b1 < 0 || ranks_above(s[e], e, s[b1], b1)) {
+                    b2 = b1;
+                    b1 = e;
+                } else if (b2 < 0 || ranks_above(s[e], e, s[b2], b2)) {
+                    b2 = e;
+                }
+            }
+            gsc[c] = (n_top == 1) ? s[b1] : s[b1] + s[b2];
+            kept[c] = 0;
+        }
+        for (int r = 0; r < TG; ++r) {
+            int best = -1;
+            for (int c = 0; c < G; ++c)
+                if (!kept[c] && (best < 0 || ranks_above(gsc[c], c, gsc[best], best)))
+                    best = c;
+            kept[best] = 1;
+        }
+
+        /* top-k among the eligible experts, best first */
+        memset(taken, 0, (size_t)El);
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < El; ++e)
+                if (kept[e / gs] && !taken[e] && (best < 0 || ranks_above(s[e], e, s[best], best)))
+                    best = e;
+            taken[best] = 1;
+            sel[j] = best;
+            ws[j] = s[best];
+        }
+
+        /* weights: the chosen scores, optionally divided by their binary32
+         * sum taken in ascending j (left as they are when that sum is 0) */
+        if (renorm) {
+            float sum = 0.0f;
+            for (int j = 0; j < k; ++j)
+                sum += ws[j];
+            if (sum > 0.0f)
+                for (int j = 0; j < k; ++j)
+                    ws[j] = ws[j] / sum;
+        }
+
+        /* redundant experts: logical expert l has replicas
+         * rep_slots[rep_off[l] .. rep_off[l+1]); token t takes replica
+         * t mod (their number); no replica gives -1, an invalid index */
+        for (int j = 0; j < k; ++j) {
+            const int l = sel[j];
+            int32_t phys = l;
+            if (rep_off) {
+                const int n = rep_off[l + 1] - rep_off[l];
+                phys = n > 0 ? rep_slots[rep_off[l] + t % n] : -1;
+            }
+            idx[(int64_t)t * k + j] = phys;
+            w[(int64_t)t * k + j] = ws[j];
+        }
+    }
+    free(z);
+    free(s);
+    free(ex);
+    free(gsc);
+    free(kept);
+    free(taken);
+    free(sel);
+    free(ws);
+    return 0;
+}

@@ -10,6 +10,8 @@
  *   [Perplexity blog]  "Lower latency and higher throughput with multi-node
  *                      DeepSeek deployment" (Perplexity, Icelandic rendering)
  *   [torchtitan PR]    "Integrate DeepEP to experimental torchtitan"
+ *   [EPLB page]        "DeepSeek V3/R1 ... DualPipe, EPLB, Profile-Data"
+ *                      (GeekNews, Turkish)
  *
  * Notation: T tokens, H hidden, k top-k, E experts, R simulated ranks,
  * El = E/R experts per rank, P = T*k (token, slot) pairs, p = t*k + j.
@@ -110,6 +112,30 @@ void oracle_combine_backward(int T, int H, int k, int E, int R, const int32_t *i
 void oracle_silu_mul_row(int I, const uint16_t *row, float *a);
 void oracle_silu_mul_quant_row(int I, const uint16_t *row, uint8_t *q, float *s);
 void oracle_quantize_f32_row(int n, const float *a, uint8_t *q, float *s);
+
+/* Router ([Perplexity blog], "MoE-beirari": one router serves every MoE
+ * model, DeepSeek's group-limited top-k with Mixtral as the case where the
+ * top-k group is all experts, and it emits top-k indices and scores;
+ * [EPLB page]: group-limited expert routing and redundant experts;
+ * [torchtitan PR]: node-limited routing).  logits [T, El] binary32, El
+ * logical experts in G groups of El/G consecutive ids.  Per token t:
+ *   z[e] = logits[t][e] + bias[e]   (one binary32 add; bias may be NULL);
+ *   s[e] = RN32(gate(z)) with the gate in binary64: softmax (gate 0,
+ *          exp(z_e - max z) / sum_e exp(z_e - max z), sum in ascending e) or
+ *          sigmoid (gate 1, 1 / (1 + exp(-z_e)));
+ *   group score = best s in the group (group_topn 1) or the binary32 sum of
+ *          the two best (group_topn 2); the TG best groups stay eligible;
+ *   the k best eligible experts in descending order; ties of scores (compared
+ *          as unsigned bit patterns) go to the lower id;
+ *   w[t][j] = s of expert j, divided by the binary32 sum over j (ascending)
+ *          when renorm and that sum is > 0;
+ *   idx[t][j] = rep_slots[rep_off[l] + t mod n_l], n_l = rep_off[l+1] -
+ *          rep_off[l] (-1 when n_l = 0), or l itself when rep_off is NULL.
+ * Returns 1 (outputs untouched) unless 1 <= k <= El, G | El, 1 <= TG <= G,
+ * k <= TG*El/G, gate in {0,1}, group_topn in {1,2}. */
+int oracle_route(int T, int El, int k, int gate, int G, int TG, int group_topn, int renorm,
+                 const float *logits, const float *bias, const int32_t *rep_off,
+                 const int32_t *rep_slots, int32_t *idx, float *w);
 
 /* Codecs. */
 uint8_t  oracle_e4m3_encode(float v);

@@ -25,8 +25,11 @@ outputs used by combine come from default_rng(seed + 1)):
   * top-k by a stable descending sort, so ties go to the lower expert id;
   * weights: the chosen gate scores, renormalized to sum 1 where the workload
     says so.
-The gates and routing are inputs, not part of the path: both the HIP path and
-the oracle consume the same arrays.
+For the dispatch / combine rows the gates and routing are inputs: both the
+HIP path and the oracle consume the same arrays.  The router's own inputs
+(unbiased logits, the Zipf bias, the group parameters and the replica table
+as CSR offsets / slot lists) are kept in Workload.extra for the on-device
+router, which recomputes the routing from them.
 """
 from __future__ import annotations
 
@@ -115,14 +118,18 @@ def make_workload(name: str, seed: int = SEED, T: int | None = None) -> Workload
     rng = np.random.default_rng(seed)
     x = bf16_from_f32(rng.standard_normal((T_, H), dtype=np.float32))
     logits = rng.standard_normal((T_, El), dtype=np.float32)
-    extra = {}
+    # the router's inputs, kept for the on-device router (which recomputes the
+    # routing from them); the arrays below are derived from the same draws
+    extra = {"logits": logits, "router": dict(
+        gate=c["gate"], n_groups=c.get("n_groups", 1), topk_groups=c.get("topk_groups", 1),
+        group_topn=2, renorm=bool(c["renorm"]))}
 
     if "zipf_s" in c:
         # popularity rank pi(e) from a seeded permutation; bias -s*ln(1+pi(e))
         pi = rng.permutation(El)
         bias = (-c["zipf_s"] * np.log1p(pi.astype(np.float64))).astype(np.float32)
         logits = (logits + bias[None, :]).astype(np.float32)
-        extra["zipf_rank"] = pi
+        extra.update(zipf_rank=pi, bias=bias)
 
     score = _softmax(logits) if c["gate"] == "softmax" else _sigmoid(logits)
 
@@ -160,7 +167,10 @@ def make_workload(name: str, seed: int = SEED, T: int | None = None) -> Workload
             for j in range(k):
                 phys[t, j] = replicas[logical[t, j]][choice[t, j]]
         topk_idx = phys.astype(np.int32)
-        extra.update(slot_logical=slot_log, n_replicas=n_rep)
+        rep_offsets = np.concatenate([[0], np.cumsum(n_rep)]).astype(np.int32)
+        rep_slots = np.concatenate(replicas).astype(np.int32)
+        extra.update(slot_logical=slot_log, n_replicas=n_rep, rep_offsets=rep_offsets,
+                     rep_slots=rep_slots)
     else:
         topk_idx = logical
 
