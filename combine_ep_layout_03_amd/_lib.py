@@ -2,9 +2,9 @@
 step of layout, dispatch, un-permute and combine runs in the library's HIP
 kernels.  Torch tensors supply device memory and the stream.
 
-The functions carry the C names: ep_layout, ep_dispatch, ep_combine,
-ep_unpermute, ep_recv_capacity_rows, ep_layout_workspace_bytes,
-ep_abi_version, ep_status_string.
+The functions carry the C names (EXPORTS lists them): the router, layout,
+dispatch, combine and their fused, backward and expert-side variants, plus
+the size helpers.
 """
 from __future__ import annotations
 
@@ -18,13 +18,14 @@ LIB_PATH = os.path.join(PKG, "libep.so")
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_CAPACITY, EP_ERR_HIP = 0, 1, 2, 3, 4
 EP_DEVERR_INDEX, EP_DEVERR_ROW, EP_DEVERR_INTERNAL = 1, 2, 4
 EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3 = 0, 1
-EP_MAX_RANKS, EP_MAX_TOPK, EP_MAX_EXPERTS, EP_MAX_HIDDEN = 64, 32, 2048, 65536
+EP_MAX_RANKS, EP_MAX_TOPK, EP_MAX_EXPERTS, EP_MAX_HIDDEN, EP_MAX_GROUPS = 64, 32, 2048, 65536, 64
+EP_GATE_SOFTMAX, EP_GATE_SIGMOID = 0, 1
 
 # Every symbol include/ep.h declares.
 EXPORTS = ("ep_abi_version", "ep_status_string", "ep_recv_capacity_rows",
            "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_layout_dispatch",
            "ep_combine", "ep_combine_shared", "ep_combine_backward", "ep_silu_mul_quant",
-           "ep_unpermute")
+           "ep_unpermute", "ep_route", "ep_route_layout")
 
 
 class EpError(RuntimeError):
@@ -43,6 +44,11 @@ class ep_config(ctypes.Structure):
 class ep_layout_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("expert_counts", "expert_offsets", "rank_counts",
                                                "rank_offsets", "slot_of", "src_of", "error_flag")]
+
+
+class ep_router_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("num_logical", "gate", "num_groups", "topk_groups",
+                                              "group_topn", "renormalize")]
 
 
 _lib = None
@@ -88,6 +94,11 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.ep_silu_mul_quant.restype = ctypes.c_int32
     L.ep_silu_mul_quant.argtypes = [cfgp, hp, ctypes.c_int32, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                     ctypes.POINTER(vp), i64, vp]
+    rtp = ctypes.POINTER(ep_router_t)
+    L.ep_route.restype = ctypes.c_int32
+    L.ep_route.argtypes = [cfgp, rtp, vp, vp, vp, vp, vp, vp, vp]
+    L.ep_route_layout.restype = ctypes.c_int32
+    L.ep_route_layout.argtypes = [cfgp, rtp, vp, vp, vp, vp, vp, vp, hp, vp, vp]
     L.ep_unpermute.restype = ctypes.c_int32
     L.ep_unpermute.argtypes = [cfgp, hp, vp, ctypes.POINTER(vp), vp, i64, vp]
     return L
@@ -107,6 +118,25 @@ class Config:
         return ep_config(self.num_tokens, self.hidden, self.num_topk, self.num_experts,
                          self.num_ranks, EP_DTYPE_FP8_E4M3 if self.fp8 else EP_DTYPE_BF16,
                          self.num_workgroups)
+
+
+@dataclass
+class Router:
+    num_logical: int
+    gate: str = "sigmoid"          # "softmax" | "sigmoid"
+    n_groups: int = 1
+    topk_groups: int = 1
+    group_topn: int = 2
+    renorm: bool = True
+
+    def c(self) -> ep_router_t:
+        g = {"softmax": EP_GATE_SOFTMAX, "sigmoid": EP_GATE_SIGMOID}[self.gate]
+        return ep_router_t(self.num_logical, g, self.n_groups, self.topk_groups, self.group_topn,
+                           int(self.renorm))
+
+
+def _router(rt) -> ep_router_t:
+    return rt.c() if isinstance(rt, Router) else rt
 
 
 def _cfg(cfg) -> ep_config:
@@ -222,3 +252,19 @@ def ep_unpermute(cfg, handle, topk_idx, recv_y, out, capacity_rows, stream=None)
     _check(load().ep_unpermute(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)), _ptr(topk_idx),
                                _ptrs(recv_y), _ptr(out), int(capacity_rows), _stream(stream)),
            "ep_unpermute")
+
+
+def ep_route(cfg, router, logits, bias, replica_offsets, replica_slots, topk_idx, topk_weights,
+             stream=None) -> None:
+    _check(load().ep_route(ctypes.byref(_cfg(cfg)), ctypes.byref(_router(router)), _ptr(logits),
+                           _ptr(bias), _ptr(replica_offsets), _ptr(replica_slots), _ptr(topk_idx),
+                           _ptr(topk_weights), _stream(stream)), "ep_route")
+
+
+def ep_route_layout(cfg, router, logits, bias, replica_offsets, replica_slots, topk_idx,
+                    topk_weights, handle, workspace, stream=None) -> None:
+    _check(load().ep_route_layout(ctypes.byref(_cfg(cfg)), ctypes.byref(_router(router)),
+                                  _ptr(logits), _ptr(bias), _ptr(replica_offsets),
+                                  _ptr(replica_slots), _ptr(topk_idx), _ptr(topk_weights),
+                                  ctypes.byref(_handle(handle)), _ptr(workspace), _stream(stream)),
+           "ep_route_layout")

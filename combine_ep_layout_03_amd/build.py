@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libep.so")
 
 SOURCES = ["ep_api.cpp", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_fused.hip",
-           "ep_expert.hip"]
+           "ep_expert.hip", "ep_router.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

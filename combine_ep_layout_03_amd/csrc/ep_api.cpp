@@ -1,7 +1,8 @@
 // ep_api.cpp -- the C ABI declared in include/ep.h: host-side validation,
 // launch planning and status mapping.  Every check here is synchronous and
-// enqueues nothing when it fails; the kernels are in ep_layout.hip,
-// ep_dispatch.hip and ep_combine.hip.
+// enqueues nothing when it fails; the kernels are in the .hip files beside it
+// (layout, dispatch, combine, the fused decode path, the expert activation and
+// the router).
 #include <cstdio>
 #include <cstdlib>
 
@@ -48,6 +49,29 @@ ep_status row_call_ok(const ep_config *cfg, const ep_layout_t *h, const int32_t 
                       int64_t capacity_rows) {
   if (!config_ok(cfg) || !handle_ok(h) || !topk_idx) return EP_ERR_INVALID_ARG;
   if (capacity_rows < (int64_t)cfg->num_tokens * cfg->num_topk) return EP_ERR_CAPACITY;
+  return EP_OK;
+}
+
+bool router_ok(const ep_config *c, const ep_router_t *r, bool replicas) {
+  if (!r) return false;
+  const int32_t El = r->num_logical;
+  if (El < 1 || El > EP_MAX_EXPERTS) return false;
+  if (r->gate != EP_GATE_SOFTMAX && r->gate != EP_GATE_SIGMOID) return false;
+  if (r->num_groups < 1 || r->num_groups > EP_MAX_GROUPS || El % r->num_groups != 0) return false;
+  if (r->topk_groups < 1 || r->topk_groups > r->num_groups) return false;
+  if (r->group_topn != 1 && r->group_topn != 2) return false;
+  if (c->num_topk > El) return false;
+  if ((int64_t)c->num_topk > (int64_t)r->topk_groups * (El / r->num_groups)) return false;
+  if (!replicas && c->num_experts != El) return false;
+  return true;
+}
+
+ep_status route_call_ok(const ep_config *cfg, const ep_router_t *router, const float *logits,
+                        const int32_t *rep_off, const int32_t *rep_slots, const int32_t *topk_idx,
+                        const float *topk_w) {
+  if (!config_ok(cfg) || !logits || !topk_idx || !topk_w) return EP_ERR_INVALID_ARG;
+  if ((rep_off == nullptr) != (rep_slots == nullptr)) return EP_ERR_INVALID_ARG;
+  if (!router_ok(cfg, router, rep_off != nullptr)) return EP_ERR_INVALID_ARG;
   return EP_OK;
 }
 
@@ -236,6 +260,32 @@ ep_status ep_unpermute(const ep_config *cfg, const ep_layout_t *h, const int32_t
   }
   trace("unpermute", cfg, ep::row_grid(*cfg, (int64_t)cfg->num_tokens * cfg->num_topk));
   return from_hip(ep::launch_unpermute(*cfg, *h, topk_idx, ry, out, capacity_rows, stream));
+}
+
+ep_status ep_route(const ep_config *cfg, const ep_router_t *router, const float *logits,
+                   const float *bias, const int32_t *replica_offsets,
+                   const int32_t *replica_slots, int32_t *topk_idx, float *topk_weights,
+                   hipStream_t stream) {
+  const ep_status st = route_call_ok(cfg, router, logits, replica_offsets, replica_slots,
+                                     topk_idx, topk_weights);
+  if (st != EP_OK) return st;
+  trace("route", cfg, ep::row_grid(*cfg, cfg->num_tokens));
+  return from_hip(ep::launch_route(*cfg, *router, logits, bias, replica_offsets, replica_slots,
+                                   topk_idx, topk_weights, stream));
+}
+
+ep_status ep_route_layout(const ep_config *cfg, const ep_router_t *router, const float *logits,
+                          const float *bias, const int32_t *replica_offsets,
+                          const int32_t *replica_slots, int32_t *topk_idx, float *topk_weights,
+                          const ep_layout_t *h, void *workspace, hipStream_t stream) {
+  ep_status st = route_call_ok(cfg, router, logits, replica_offsets, replica_slots, topk_idx,
+                               topk_weights);
+  if (st != EP_OK) return st;
+  if (!handle_ok(h) || !workspace) return EP_ERR_INVALID_ARG;
+  st = ep_route(cfg, router, logits, bias, replica_offsets, replica_slots, topk_idx, topk_weights,
+                stream);
+  if (st != EP_OK) return st;
+  return ep_layout(cfg, topk_idx, h, workspace, stream);
 }
 
 }  // extern "C"

@@ -26,7 +26,10 @@
  *                      work from the upper-bound buffer).
  *   [torchtitan PR]    "Integrate DeepEP to experimental torchtitan" (the
  *                      token unpermute after the experts; index selection on
- *                      the host costs CPU time).
+ *                      the host costs CPU time; node-limited routing).
+ *   [EPLB page]        "DeepSeek V3/R1 ... DualPipe, EPLB, Profile-Data"
+ *                      (GeekNews, Turkish): redundant (replicated) experts
+ *                      and group-limited expert routing.
  *
  * Model.  One GPU.  The R expert-parallel "ranks" are R destination buffers in
  * the same HBM; rank r owns the experts [r*E/R, (r+1)*E/R).  A (token t, top-k
@@ -71,6 +74,7 @@ extern "C" {
 #define EP_MAX_TOPK 32     /* k */
 #define EP_MAX_EXPERTS 2048 /* E: the layout keeps per-expert counters in LDS */
 #define EP_MAX_HIDDEN 65536 /* H */
+#define EP_MAX_GROUPS 64    /* router expert groups: one per lane of a wave */
 
 typedef int32_t ep_status;
 #define EP_OK 0
@@ -87,6 +91,10 @@ typedef int32_t ep_status;
 typedef int32_t ep_dtype;
 #define EP_DTYPE_BF16 0     /* dispatch copies bf16 rows */
 #define EP_DTYPE_FP8_E4M3 1 /* dispatch quantizes rows to E4M3 + fp32 scales */
+
+typedef int32_t ep_gate;
+#define EP_GATE_SOFTMAX 0 /* softmax over the token's logical experts */
+#define EP_GATE_SIGMOID 1 /* independent sigmoid per expert */
 
 typedef struct {
   int32_t num_tokens;     /* T >= 1 (cf. num_max_tokens_per_rank of the buffer) */
@@ -113,6 +121,17 @@ typedef struct {
   int32_t *src_of;         /* [T*k] global slot -> pair p (inverse of slot_of) */
   int32_t *error_flag;     /* [1]   EP_DEVERR_* bits, 0 = ok */
 } ep_layout_t;
+
+/* Router parameters (see ep_route).  Node-limited routing is group-limited
+ * routing with one group per node's experts. */
+typedef struct {
+  int32_t num_logical;  /* El in [1, EP_MAX_EXPERTS]: experts the router scores */
+  int32_t gate;         /* ep_gate */
+  int32_t num_groups;   /* G in [1, EP_MAX_GROUPS], El % G == 0; 1 = plain top-k */
+  int32_t topk_groups;  /* TG in [1, G]: groups a token may use; k <= TG * El/G */
+  int32_t group_topn;   /* 1: a group scores its best expert; 2: its two best, summed */
+  int32_t renormalize;  /* nonzero: weights divided by their sum over the k chosen */
+} ep_router_t;
 
 /* EP_ABI_VERSION of the loaded library. */
 uint32_t ep_abi_version(void);
@@ -240,6 +259,45 @@ ep_status ep_silu_mul_quant(const ep_config *cfg /*(host)*/, const ep_layout_t *
                             int32_t intermediate, const void *const *act_in /*(host)[R]*/,
                             void *const *q_out /*(host)[R]*/, float *const *scales_out /*(host)[R]*/,
                             int64_t capacity_rows, hipStream_t stream);
+
+/* Router ([Perplexity blog] "MoE-beirari": one router for every MoE model,
+ * DeepSeek's group-limited top-k with Mixtral's as the case of one group
+ * holding all experts, emitting top-k indices and scores per token;
+ * [EPLB page]: group-limited routing and redundant experts; [torchtitan PR]:
+ * node-limited routing).  For each token t, with logits [T, El] fp32:
+ *   z[e] = logits[t][e] + bias[e]  (one fp32 add; bias [El] may be NULL);
+ *   s[e] = gate score evaluated in binary64 and rounded once to fp32:
+ *          softmax exp(z_e - max z) / sum exp(z_i - max z), or sigmoid
+ *          1 / (1 + exp(-z_e));
+ *   each group of El/G consecutive experts scores its best s (group_topn 1)
+ *          or the fp32 sum of its two best; the TG best groups stay eligible;
+ *   topk_idx[t] = the k best eligible experts, best first; equal scores
+ *          (compared as fp32 bit patterns) go to the lower id;
+ *   topk_weights[t][j] = s of expert j, divided by the fp32 sum over j
+ *          (ascending) when renormalize is set and that sum is > 0.
+ * Redundant experts: with replica_offsets [El+1] and replica_slots (device
+ * arrays, CSR), logical expert l is served by physical experts
+ * replica_slots[replica_offsets[l] ..  replica_offsets[l+1]) and token t
+ * takes the (t mod count)-th; a logical expert with no replica yields -1,
+ * and a slot outside [0, E) is passed through, so ep_layout flags either with
+ * EP_DEVERR_INDEX.  Without a table (both NULL) topk_idx holds logical ids and
+ * cfg->num_experts must equal El.  Logits must be finite (otherwise the
+ * choice is unspecified but still k distinct experts).  cfg->hidden and
+ * num_ranks are checked as everywhere but not used.  One launch, one wave
+ * per token. */
+ep_status ep_route(const ep_config *cfg /*(host)*/, const ep_router_t *router /*(host)*/,
+                   const float *logits, const float *bias, const int32_t *replica_offsets,
+                   const int32_t *replica_slots, int32_t *topk_idx, float *topk_weights,
+                   hipStream_t stream);
+
+/* ep_route followed by ep_layout on its output ([Perplexity blog]
+ * "MoE-beirari": the dense dispatch and combine need the routing summed per
+ * expert), so the handle is built from the logits with no host round trip.
+ * Arguments as for the two calls; `workspace` as for ep_layout. */
+ep_status ep_route_layout(const ep_config *cfg /*(host)*/, const ep_router_t *router /*(host)*/,
+                          const float *logits, const float *bias, const int32_t *replica_offsets,
+                          const int32_t *replica_slots, int32_t *topk_idx, float *topk_weights,
+                          const ep_layout_t *h /*(host)*/, void *workspace, hipStream_t stream);
 
 /* Un-permute ([torchtitan PR]: the token unpermute after the experts) as a
  * standalone call for testing: out[p] (H bf16) := recv_y[r(p)] row row(p), so

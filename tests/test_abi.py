@@ -48,12 +48,13 @@ def test_header_constants_match_binding():
     for name in ("EP_OK", "EP_ERR_INVALID_ARG", "EP_ERR_UNSUPPORTED", "EP_ERR_CAPACITY",
                  "EP_ERR_HIP", "EP_DEVERR_INDEX", "EP_DEVERR_ROW", "EP_DEVERR_INTERNAL", "EP_DTYPE_BF16",
                  "EP_DTYPE_FP8_E4M3", "EP_MAX_RANKS", "EP_MAX_TOPK", "EP_MAX_EXPERTS",
-                 "EP_MAX_HIDDEN"):
+                 "EP_MAX_HIDDEN", "EP_MAX_GROUPS", "EP_GATE_SOFTMAX", "EP_GATE_SIGMOID"):
         assert int(consts[name]) == getattr(_lib, name), name
     assert int(consts["EP_ABI_VERSION"]) == ep.ep_abi_version()
     # struct layouts: 7 int32 fields, 7 pointers
     assert ctypes.sizeof(_lib.ep_config) == 28
     assert ctypes.sizeof(_lib.ep_layout_t) == 56
+    assert ctypes.sizeof(_lib.ep_router_t) == 24
 
 
 def test_status_strings(lib):
@@ -124,6 +125,49 @@ def test_null_pointers_and_capacity_rejected_before_any_launch(lib):
     assert ei.value.status == ep.EP_ERR_CAPACITY
     with pytest.raises(ep.EpError) as ei:
         ep.ep_unpermute(c, h, 8, [8, None, 8, 8], 8, 32, 0)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad_router,bad_cfg,replicas", [
+    (dict(num_logical=0), {}, False), (dict(num_logical=4096), {}, False),
+    (dict(gate=2), {}, False), (dict(num_groups=3), {}, False),
+    (dict(num_groups=128, num_logical=256), dict(num_experts=256), False),
+    (dict(num_groups=4, topk_groups=0), {}, False), (dict(num_groups=4, topk_groups=5), {}, False),
+    (dict(group_topn=0), {}, False), (dict(group_topn=3), {}, False),
+    (dict(num_groups=8, topk_groups=1), dict(num_topk=3), False),  # k > TG * El/G = 2
+    (dict(num_logical=8), {}, False),                              # E != El without replicas
+    (dict(), dict(num_topk=17, num_experts=32), True),             # k > El
+])
+def test_router_parameters_rejected(lib, bad_router, bad_cfg, replicas):
+    base = dict(num_tokens=16, hidden=256, num_topk=2, num_experts=16, num_ranks=4)
+    base.update(bad_cfg)
+    c = ep.Config(**base)
+    r = dict(num_logical=16, gate=1, num_groups=1, topk_groups=1, group_topn=2, renormalize=1)
+    r.update(bad_router)
+    rt = _lib.ep_router_t(*r.values())
+    rep = (8, 8) if replicas else (None, None)
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_route(c, rt, 8, None, rep[0], rep[1], 8, 8, 0)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_route_layout(c, rt, 8, None, rep[0], rep[1], 8, 8, _lib.ep_layout_t(*([8] * 7)), 8, 0)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+
+
+def test_router_null_pointers_rejected(lib):
+    c = ep.Config(16, 256, 2, 16, 4)
+    rt = ep.Router(16).c()
+    for args in [(None, None, None, None, 8, 8), (8, None, None, None, None, 8),
+                 (8, None, None, None, 8, None), (8, None, 8, None, 8, 8),
+                 (8, None, None, 8, 8, 8)]:
+        with pytest.raises(ep.EpError) as ei:
+            ep.ep_route(c, rt, *args, 0)
+        assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    with pytest.raises(ep.EpError) as ei:   # handle with a NULL array
+        ep.ep_route_layout(c, rt, 8, None, None, None, 8, 8, _lib.ep_layout_t(*([8] * 6 + [None])), 8, 0)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    with pytest.raises(ep.EpError) as ei:   # no workspace
+        ep.ep_route_layout(c, rt, 8, None, None, None, 8, 8, _lib.ep_layout_t(*([8] * 7)), None, 0)
     assert ei.value.status == ep.EP_ERR_INVALID_ARG
 
 
