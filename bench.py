@@ -70,8 +70,9 @@ def source_sha(paths):
 
 def kernel_sources():
     c = os.path.join(ROOT, "combine_ep_layout_03_amd", "csrc")
-    return {"combine": [os.path.join(c, "ep_combine.hip"), os.path.join(c, "ep_internal.h")],
-            "dispatch": [os.path.join(c, "ep_dispatch.hip"), os.path.join(c, "ep_internal.h")]}
+    common = [os.path.join(c, "ep_internal.h"), os.path.join(c, "ep_device.h")]
+    return {"combine": [os.path.join(c, "ep_combine.hip")] + common,
+            "dispatch": [os.path.join(c, "ep_dispatch.hip")] + common}
 
 
 def load_traffic(kernel, workload):
@@ -204,7 +205,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip timing combine_shared and combine_backward")
+                    help="skip timing the other entry points (router, decode-style, backward, expert-side)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph and replayed")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -392,6 +393,46 @@ def main():
         assert int(h.error_flag.item()) == 0
         del shared, gout, grows, gwt, act, aq, asc
 
+        # the router on this workload's logits, into buffers of its own: alone,
+        # feeding the layout, and the whole step from logits (route + layout +
+        # dispatch + combine)
+        rin = w.extra
+        El = rin["logits"].shape[1]
+        logits_d = up(rin["logits"])
+        opt = lambda key: up(rin[key]) if key in rin else None
+        bias_d, ro_d, rsl_d = opt("bias"), opt("rep_offsets"), opt("rep_slots")
+        dp = lambda t: None if t is None else t.data_ptr()
+        crt = ep.Router(El, **rin["router"]).c()
+        prt = ctypes.byref(crt)
+        idx2, w2 = torch.empty_like(idx), torch.empty_like(wts)
+        h2 = Handle.alloc(cfg, dev)
+        ws2 = alloc_workspace(cfg, dev)
+        ch2 = _lib.ep_layout_t(*[getattr(h2, n).data_ptr() for n, _ in _lib.ep_layout_t._fields_])
+        ph2 = ctypes.byref(ch2)
+        rt_args = (pc, prt, logits_d.data_ptr(), dp(bias_d), dp(ro_d), dp(rsl_d), idx2.data_ptr(),
+                   w2.data_ptr())
+        rcall = lambda: L.ep_route(*rt_args, sp)
+        rlcall = lambda: L.ep_route_layout(*rt_args, ph2, ws2.data_ptr(), sp)
+        route_bytes = (w.T * El * 4 + w.T * w.k * 8 + (El * 4 if bias_d is not None else 0)
+                       + (w.T * w.k * 8 if ro_d is not None else 0))
+        for name, fn, nbytes in (("route", rcall, route_bytes),
+                                 ("route_layout", rlcall, route_bytes + algorithmic_bytes(
+                                     w.T, w.H, w.k, w.E, w.R, w.fp8)["layout"])):
+            for _ in range(3):
+                assert fn() == 0
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(min(K, 20))]
+            for a, b_ in evs:
+                a.record(stream)
+                assert fn() == 0
+                b_.record(stream)
+            torch.cuda.synchronize()
+            us = statistics.median(a.elapsed_time(b_) * 1e3 for a, b_ in evs)
+            extras[name] = {"us": round(us, 2), "algorithmic_bytes": nbytes,
+                            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        assert int(h2.error_flag.item()) == 0
+        assert torch.equal(idx2, idx) and torch.equal(h2.slot_of, h.slot_of)
+
         # decode-style steps: the one-call layout + dispatch, and the cached-
         # handle step (gating unchanged: dispatch + combine, no layout)
         def step_time(fns):
@@ -416,6 +457,10 @@ def main():
         extras["layout_dispatch_us"] = round(step_time([ld]), 2)
         extras["fused_step_us"] = round(step_time([ld, cc]), 2)
         extras["cached_handle_step_us"] = round(step_time([cd, cc]), 2)
+        rd = lambda: L.ep_dispatch(pc, ph2, idx2.data_ptr(), x.data_ptr(), rx, rs, cap, sp)
+        rc = lambda: L.ep_combine(pc, ph2, idx2.data_ptr(), ry, w2.data_ptr(), out.data_ptr(), cap, sp)
+        extras["routed_step_us"] = round(step_time([rlcall, rd, rc]), 2)
+        assert int(h2.error_flag.item()) == 0
         assert int(h.error_flag.item()) == 0
 
     graph_us = None

@@ -10,20 +10,21 @@
 // (node-limited routing).
 //
 // Design.  A single-wave workgroup takes one token at a time (grid-stride).
-// Lane l holds experts l, l+64, ... (coalesced loads of the logit row).  The
-// gate is evaluated in binary64 and rounded once to binary32, so the scores
-// -- and with them every selection, which compares binary32 values only --
-// do not depend on how a device or host libm rounds its exp; the binary64
-// softmax denominator is a wave butterfly sum.  The scores go to LDS.  Lanes
-// below G score one group each (its best, or the sum of its two best); TG
-// rounds of a wave-wide maximum over 64-bit keys (score bits above the
-// complement of the id, so equal scores favour the lower id) pick the
-// eligible groups, and k more rounds pick the experts, each lane keeping the
-// best key of its own experts and rescanning only when its key was taken.
-// Lane j ends with pick j; renormalization sums the k picks in order with
-// readlane, so the weights are the same binary32 operations as a sequential
-// loop.  fp contraction is off in this file: the scores are exact
-// compositions of correctly rounded operations.
+// Lane l holds the NPER consecutive experts [l*NPER, (l+1)*NPER) in
+// registers (NPER a power of two, 64*NPER >= El).  The gate is evaluated in
+// binary64 and rounded once to binary32, so the scores -- and with them every
+// selection, which compares binary32 values only -- do not depend on how a
+// device or host libm rounds its exp.  Scores are non-negative, so their bit
+// patterns order like the values; a wave maximum of 32-bit patterns is four
+// DPP steps inside each row of 16 lanes, four readlanes and a scalar max, and
+// a ballot of the lanes holding that maximum names the winner: the lowest such
+// lane holds the lowest expert id, which is the tie rule.  Groups whose
+// experts cover whole, power-of-two runs of lanes are scored by a top-2 merge
+// across those lanes; other shapes stage the scores in LDS and let lane c
+// score group c.  Renormalization sums the k picks in order with readlane, so
+// the weights are the same binary32 operations as a sequential loop.  fp
+// contraction is off: the scores are exact compositions of correctly rounded
+// operations.
 #include <math.h>
 
 #include "ep_device.h"
@@ -36,133 +37,252 @@ namespace {
 
 using namespace dev;
 
-__device__ inline uint64_t rank_key(float s, int id) {
-  return ((uint64_t)__float_as_uint(s) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
-}
-__device__ inline int key_id(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
-__device__ inline float key_score(uint64_t key) { return __uint_as_float((uint32_t)(key >> 32)); }
+// DPP controls (gfx9): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror,
+// row_mirror.  After these four steps every lane of a 16-lane row holds the
+// row's reduction.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
-__device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o, kWave);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o, kWave);
-    const uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
+template <int CTRL>
+__device__ inline uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-__device__ inline double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+__device__ inline uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ inline uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+__device__ inline uint32_t rdl(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+// Maximum over the wave (unsigned), uniform result.
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = umax(v, dpp<kDppXor1>(v));
+  v = umax(v, dpp<kDppXor2>(v));
+  v = umax(v, dpp<kDppHalfMirror>(v));
+  v = umax(v, dpp<kDppMirror>(v));
+  return umax(umax(rdl(v, 0), rdl(v, 16)), umax(rdl(v, 32), rdl(v, 48)));
 }
 
 __device__ inline float wave_max_f32(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, __uint_as_float(dpp<kDppXor1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kDppXor2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kDppHalfMirror>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kDppMirror>(__float_as_uint(v))));
+  const float a = fmaxf(__uint_as_float(rdl(__float_as_uint(v), 0)),
+                        __uint_as_float(rdl(__float_as_uint(v), 16)));
+  const float b = fmaxf(__uint_as_float(rdl(__float_as_uint(v), 32)),
+                        __uint_as_float(rdl(__float_as_uint(v), 48)));
+  return fmaxf(a, b);
 }
 
-// Best key among this lane's experts that are eligible and not yet taken.
-__device__ inline uint64_t lane_best(const float *s, int lane, int El, int gs, uint64_t kept,
-                                     uint32_t taken) {
-  uint64_t best = 0;
-  for (int i = 0, e = lane; e < El; ++i, e += kWave) {
-    if ((taken >> i) & 1u) continue;
-    if (!((kept >> (e / gs)) & 1ull)) continue;
-    const uint64_t key = rank_key(s[e], e);
-    best = key > best ? key : best;
+template <int CTRL>
+__device__ inline double dpp_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = dpp<CTRL>((uint32_t)u), hi = dpp<CTRL>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+__device__ inline double rdl_f64(double v, int lane) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  return __longlong_as_double(
+      (long long)(((uint64_t)rdl((uint32_t)(u >> 32), lane) << 32) | rdl((uint32_t)u, lane)));
+}
+
+// Sum over the wave in binary64 (a fixed tree), uniform result.
+__device__ inline double wave_sum_f64(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
+  return (rdl_f64(v, 0) + rdl_f64(v, 16)) + (rdl_f64(v, 32) + rdl_f64(v, 48));
+}
+
+// Value of lane (lane ^ off) for off a power of two below 64.
+__device__ inline uint32_t xor_lane(uint32_t v, int off) {
+  switch (off) {
+    case 1: return dpp<kDppXor1>(v);
+    case 2: return dpp<kDppXor2>(v);
+    default: return (uint32_t)__shfl_xor((int)v, off, kWave);
   }
-  return best;
 }
 
+// Winner among the lanes that offer `bits` (has == true): the largest bits,
+// then the lowest lane.  Returns -1 when no lane offers.
+__device__ inline int wave_pick(bool has, uint32_t bits, uint32_t &best_bits) {
+  const uint32_t mx = wave_max_u32(has ? bits : 0u);
+  const uint64_t b = __ballot(has && bits == mx);
+  best_bits = mx;
+  return b ? (int)__builtin_ctzll(b) : -1;
+}
+
+template <int NPER>
 __global__ __launch_bounds__(kWave) void route_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias,
     const int32_t *__restrict__ rep_off, const int32_t *__restrict__ rep_slots, int32_t T,
     int32_t El, int32_t k, int32_t gate, int32_t G, int32_t TG, int32_t topn, int32_t renorm,
     int32_t *__restrict__ idx, float *__restrict__ wout) {
-  extern __shared__ double lds[];
-  double *ex = lds;                                               // [El] softmax numerators
-  float *s = reinterpret_cast<float *>(lds + (gate == EP_GATE_SOFTMAX ? El : 0));  // [El]
+  extern __shared__ float lds_s[];  // [El], only for groups that split a lane's experts
   const int lane = threadIdx.x;
+  const int e0 = lane * NPER;
   const int gs = El / G;
+  const int lpg = gs / NPER;  // lanes per group on the register path
+  const bool lane_groups = G > 1 && gs % NPER == 0 && (lpg & (lpg - 1)) == 0;
+  const bool vec = NPER >= 4 && (El & 3) == 0 && (((uintptr_t)logits) & 15u) == 0 &&
+                   (!bias || (((uintptr_t)bias) & 15u) == 0);
+  uint32_t valid = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) valid |= (e0 + i < El) ? 1u << i : 0u;
+
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
     const float *zr = logits + t * (int64_t)El;
+    float z[NPER];
+    if (vec) {
+#pragma unroll
+      for (int i = 0; i < NPER; i += 4) {
+        float4 v = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+        if (e0 + i < El) {
+          v = *reinterpret_cast<const float4 *>(zr + e0 + i);
+          if (bias) b = *reinterpret_cast<const float4 *>(bias + e0 + i);
+        }
+        z[i] = bias ? v.x + b.x : v.x;
+        z[i + 1] = bias ? v.y + b.y : v.y;
+        z[i + 2] = bias ? v.z + b.z : v.z;
+        z[i + 3] = bias ? v.w + b.w : v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        const int e = e0 + i;
+        z[i] = e < El ? (bias ? zr[e] + bias[e] : zr[e]) : 0.0f;
+      }
+    }
+
+    // gate scores: binary64, rounded once
+    float s[NPER];
     if (gate == EP_GATE_SOFTMAX) {
       float m = -INFINITY;
-      for (int e = lane; e < El; e += kWave) {
-        const float z = bias ? zr[e] + bias[e] : zr[e];
-        s[e] = z;  // the logit, until the score replaces it
-        m = fmaxf(m, z);
-      }
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        if ((valid >> i) & 1u) m = fmaxf(m, z[i]);
       m = wave_max_f32(m);
+      double ex[NPER];
       double sum = 0.0;
-      for (int e = lane; e < El; e += kWave) {
-        const double x = exp((double)s[e] - (double)m);
-        ex[e] = x;
-        sum += x;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        ex[i] = ((valid >> i) & 1u) ? exp((double)z[i] - (double)m) : 0.0;
+        sum += ex[i];
       }
       sum = wave_sum_f64(sum);
-      for (int e = lane; e < El; e += kWave) s[e] = (float)(ex[e] / sum);
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) s[i] = (float)(ex[i] / sum);
     } else {
-      for (int e = lane; e < El; e += kWave) {
-        const float z = bias ? zr[e] + bias[e] : zr[e];
-        s[e] = (float)(1.0 / (1.0 + exp(-(double)z)));
-      }
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) s[i] = (float)(1.0 / (1.0 + exp(-(double)z[i])));
     }
-    __syncthreads();
 
-    // eligible groups (bit c of kept); one group keeps every expert
-    uint64_t kept = ~0ull;
-    if (G > 1) {
-      uint64_t gkey = 0;
-      if (lane < G) {
-        uint64_t k1 = 0, k2 = 0;
-        for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
-          const uint64_t key = rank_key(s[e], e);
-          if (key > k1) {
-            k2 = k1;
-            k1 = key;
-          } else if (key > k2) {
-            k2 = key;
-          }
+    // eligible experts (bit i of elig): every valid one, or those of the TG
+    // best groups
+    uint32_t elig = valid;
+    if (lane_groups) {
+      // this lane's two best, then a top-2 merge across the group's lanes
+      uint32_t a1 = 0, a2 = 0;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        const uint32_t b = __float_as_uint(s[i]);
+        if ((valid >> i) & 1u) {
+          a2 = umax(a2, umin(a1, b));
+          a1 = umax(a1, b);
         }
-        const float g = (topn == 1 || gs == 1) ? key_score(k1) : key_score(k1) + key_score(k2);
-        gkey = rank_key(g, lane);
       }
-      kept = 0;
+      for (int off = 1; off < lpg; off <<= 1) {
+        const uint32_t b1 = xor_lane(a1, off), b2 = xor_lane(a2, off);
+        a2 = umax(umin(a1, b1), umax(a2, b2));
+        a1 = umax(a1, b1);
+      }
+      const int grp = lane / lpg;
+      const float g = (topn == 1 || gs == 1) ? __uint_as_float(a1)
+                                             : __uint_as_float(a1) + __uint_as_float(a2);
+      bool offer = (lane % lpg) == 0 && grp < G;
+      uint64_t kept = 0;
       for (int r = 0; r < TG; ++r) {
-        const uint64_t best = wave_max_u64(gkey);
-        const int c = key_id(best);
-        kept |= 1ull << c;
-        if (lane == c) gkey = 0;
+        uint32_t bb;
+        const int wl = wave_pick(offer, __float_as_uint(g), bb);
+        if (wl < 0) break;
+        kept |= 1ull << (wl / lpg);
+        if (lane == wl) offer = false;
       }
+      elig = ((kept >> grp) & 1ull) ? valid : 0u;
+    } else if (G > 1) {
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        if ((valid >> i) & 1u) lds_s[e0 + i] = s[i];
+      __syncthreads();
+      float g = 0.0f;
+      if (lane < G) {
+        uint32_t a1 = 0, a2 = 0;
+        for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
+          const uint32_t b = __float_as_uint(lds_s[e]);
+          a2 = umax(a2, umin(a1, b));
+          a1 = umax(a1, b);
+        }
+        g = (topn == 1 || gs == 1) ? __uint_as_float(a1) : __uint_as_float(a1) + __uint_as_float(a2);
+      }
+      bool offer = lane < G;
+      uint64_t kept = 0;
+      for (int r = 0; r < TG; ++r) {
+        uint32_t bb;
+        const int wl = wave_pick(offer, __float_as_uint(g), bb);
+        if (wl < 0) break;
+        kept |= 1ull << wl;
+        if (lane == wl) offer = false;
+      }
+      elig = 0;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        if ((valid >> i) & 1u) elig |= (uint32_t)((kept >> ((e0 + i) / gs)) & 1ull) << i;
+      __syncthreads();  // the next token rewrites lds_s
     }
 
-    // top-k: lane j keeps pick j
-    uint32_t taken = 0;
-    uint64_t mine = lane_best(s, lane, El, gs, kept, taken);
+    // top-k: each lane offers its best eligible expert; lane j keeps pick j
+    int ci = -1;
+    uint32_t cb = 0;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const uint32_t b = __float_as_uint(s[i]);
+      if (((elig >> i) & 1u) && (ci < 0 || b > cb)) {
+        ci = i;
+        cb = b;
+      }
+    }
     int32_t sel = -1;
     float ws = 0.0f;
     for (int j = 0; j < k; ++j) {
-      const uint64_t best = wave_max_u64(mine);
-      if (best == 0) break;  // fewer eligible experts than k: excluded on the host
-      const int e = key_id(best);
+      uint32_t bb;
+      const int wl = wave_pick(ci >= 0, cb, bb);
+      if (wl < 0) break;  // fewer eligible experts than k: excluded on the host
+      const int e = wl * NPER + (int)rdl((uint32_t)ci, wl);
       if (lane == j) {
         sel = e;
-        ws = key_score(best);
+        ws = __uint_as_float(bb);
       }
-      if (lane == (e % kWave)) {
-        taken |= 1u << (e / kWave);
-        mine = lane_best(s, lane, El, gs, kept, taken);
+      if (lane == wl) {
+        elig &= ~(1u << ci);
+        ci = -1;
+        cb = 0;
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) {
+          const uint32_t b = __float_as_uint(s[i]);
+          if (((elig >> i) & 1u) && (ci < 0 || b > cb)) {
+            ci = i;
+            cb = b;
+          }
+        }
       }
     }
 
     if (renorm) {
       float sum = 0.0f;
-      for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), j));
+      for (int j = 0; j < k; ++j) sum += __uint_as_float(rdl(__float_as_uint(ws), j));
       if (sum > 0.0f) ws = ws / sum;
     }
     if (lane < k) {
@@ -174,24 +294,34 @@ __global__ __launch_bounds__(kWave) void route_kernel(
       idx[t * k + lane] = phys;
       wout[t * k + lane] = ws;
     }
-    __syncthreads();  // the next token reuses the LDS scores
   }
 }
 
 }  // namespace
 
 size_t route_lds_bytes(int32_t El, int32_t gate) {
-  return (size_t)El * (gate == EP_GATE_SOFTMAX ? sizeof(double) + sizeof(float) : sizeof(float));
+  (void)gate;
+  return (size_t)El * sizeof(float);
 }
 
 hipError_t launch_route(const ep_config &c, const ep_router_t &rt, const float *logits,
                         const float *bias, const int32_t *rep_off, const int32_t *rep_slots,
                         int32_t *topk_idx, float *topk_w, hipStream_t s) {
   const int grid = row_grid(c, c.num_tokens);
-  hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(kWave), route_lds_bytes(rt.num_logical, rt.gate),
-                     s, logits, bias, rep_off, rep_slots, c.num_tokens, rt.num_logical, c.num_topk,
-                     rt.gate, rt.num_groups, rt.topk_groups, rt.group_topn, rt.renormalize,
-                     topk_idx, topk_w);
+  const size_t lds = route_lds_bytes(rt.num_logical, rt.gate);
+#define EP_ROUTE_LAUNCH(N)                                                                     \
+  hipLaunchKernelGGL(route_kernel<N>, dim3(grid), dim3(kWave), lds, s, logits, bias, rep_off, \
+                     rep_slots, c.num_tokens, rt.num_logical, c.num_topk, rt.gate,            \
+                     rt.num_groups, rt.topk_groups, rt.group_topn, rt.renormalize, topk_idx,  \
+                     topk_w)
+  const int El = rt.num_logical;
+  if (El <= 64) EP_ROUTE_LAUNCH(1);
+  else if (El <= 128) EP_ROUTE_LAUNCH(2);
+  else if (El <= 256) EP_ROUTE_LAUNCH(4);
+  else if (El <= 512) EP_ROUTE_LAUNCH(8);
+  else if (El <= 1024) EP_ROUTE_LAUNCH(16);
+  else EP_ROUTE_LAUNCH(32);
+#undef EP_ROUTE_LAUNCH
   return hipGetLastError();
 }
 
