@@ -21,6 +21,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -122,9 +123,20 @@ def cpu_baseline(workload_name, sample_tokens, min_seconds):
                       f"of {os.cpu_count()} host cores"}
 
 
-KERNEL_KEYS = {"combine": "combine_kernel", "dispatch": "dispatch_fp8_kernel",
-               "layout_count": "layout_count_kernel", "layout_scatter": "layout_scatter_kernel",
-               "layout_small": "layout_small_kernel"}
+# rocprofv3 kernel names ("ep::(anonymous namespace)::combine_kernel<false>(int const*, ...")
+# matched by anchored patterns: combine_kernel<false> is ep_combine, <true> ep_combine_shared
+KERNEL_KEYS = {
+    "combine": r"::combine_kernel(<false>)?\(",
+    "dispatch": r"::dispatch_(fp8|bf16)_kernel\(",
+    "layout_count": r"::layout_count_kernel\(",
+    "layout_scatter": r"::layout_scatter_kernel\(",
+    "layout_small": r"::layout_small_kernel\(",
+    "route": r"::route_kernel<\d+>\(",
+    "layout_dispatch_small": r"::layout_dispatch_small_kernel<(true|false)>\(",
+    "combine_shared": r"::combine_kernel<true>\(",
+    "combine_backward": r"::combine_backward_kernel\(",
+    "silu_mul_quant": r"::silu_mul_quant_kernel\(",
+}
 CAL_COPY_KEY = "bitwise_not"      # elementwise kernel: reads and writes CAL_BYTES
 CAL_FILL_KEY = "FillFunctor<unsigned char>"  # writes CAL_BYTES
 
@@ -146,12 +158,13 @@ def summarize(trace_dir, fetch_dir, write_dir, workload, command_prefix):
     fetch = one(fetch_dir, "_counter_collection.csv")
     write = one(write_dir, "_counter_collection.csv")
 
-    def per_kernel(rows, key):
-        v = [float(r["Counter_Value"]) for r in rows if key in r["Kernel_Name"]]
+    def per_kernel(rows, key, regex=True):
+        hit = (lambda n: re.search(key, n)) if regex else (lambda n: key in n)
+        v = [float(r["Counter_Value"]) for r in rows if hit(r["Kernel_Name"])]
         return statistics.median(v) if v else None
 
-    fetch_cal = per_kernel(fetch, CAL_COPY_KEY)     # KiB read by a CAL_BYTES-read kernel
-    write_cal = per_kernel(write, CAL_FILL_KEY)     # KiB written by a CAL_BYTES-write kernel
+    fetch_cal = per_kernel(fetch, CAL_COPY_KEY, False)  # KiB read by a CAL_BYTES-read kernel
+    write_cal = per_kernel(write, CAL_FILL_KEY, False)  # KiB written by a CAL_BYTES-write kernel
     f_fetch = CAL_BYTES / fetch_cal
     f_write = CAL_BYTES / write_cal
     cmd_trace = f"{command_prefix} rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o {workload} -- python3 bench.py --config {workload} --steps 20 --warmup 3 --skip-cpu"
@@ -168,7 +181,8 @@ def summarize(trace_dir, fetch_dir, write_dir, workload, command_prefix):
              "|---|---|---|---|---|---|---|"]
     traffic = {}
     for short, key in KERNEL_KEYS.items():
-        st = [r for r in stats if key in r["Name"]]
+        st = [r for r in stats if re.search(key, r["Name"])]
+        assert len(st) <= 1, (short, [r["Name"][:80] for r in st])
         if not st:
             continue
         r = st[0]
