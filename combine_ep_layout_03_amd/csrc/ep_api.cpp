@@ -34,6 +34,9 @@ bool handle_ok(const ep_layout_t *h) {
          h->slot_of && h->src_of && h->error_flag;
 }
 
+// The layout reads its chunk table with 16-byte loads.
+bool workspace_ok(const void *ws) { return ws && ((uintptr_t)ws & 15u) == 0; }
+
 ep_status from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
 
 void trace(const char *what, const ep_config *c, int grid) {
@@ -105,7 +108,8 @@ size_t ep_layout_workspace_bytes(const ep_config *cfg) {
 
 ep_status ep_layout(const ep_config *cfg, const int32_t *topk_idx, const ep_layout_t *h,
                     void *workspace, hipStream_t stream) {
-  if (!config_ok(cfg) || !handle_ok(h) || !topk_idx || !workspace) return EP_ERR_INVALID_ARG;
+  if (!config_ok(cfg) || !handle_ok(h) || !topk_idx || !workspace_ok(workspace))
+    return EP_ERR_INVALID_ARG;
   const ep::LayoutPlan plan =
       ep::plan_layout((int64_t)cfg->num_tokens * cfg->num_topk, cfg->num_experts);
   if (debug_enabled())
@@ -140,7 +144,8 @@ ep_status ep_layout_dispatch(const ep_config *cfg, const int32_t *topk_idx, cons
                              void *workspace, const void *x, void *const *recv_x,
                              float *const *recv_scales, int64_t capacity_rows,
                              hipStream_t stream) {
-  if (!config_ok(cfg) || !handle_ok(h) || !topk_idx || !workspace) return EP_ERR_INVALID_ARG;
+  if (!config_ok(cfg) || !handle_ok(h) || !topk_idx || !workspace_ok(workspace))
+    return EP_ERR_INVALID_ARG;
   ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
   if (st != EP_OK) return st;
   if (!x || !recv_x) return EP_ERR_INVALID_ARG;
@@ -281,7 +286,7 @@ ep_status ep_route_layout(const ep_config *cfg, const ep_router_t *router, const
   ep_status st = route_call_ok(cfg, router, logits, replica_offsets, replica_slots, topk_idx,
                                topk_weights);
   if (st != EP_OK) return st;
-  if (!handle_ok(h) || !workspace) return EP_ERR_INVALID_ARG;
+  if (!handle_ok(h) || !workspace_ok(workspace)) return EP_ERR_INVALID_ARG;
   st = ep_route(cfg, router, logits, bias, replica_offsets, replica_slots, topk_idx, topk_weights,
                 stream);
   if (st != EP_OK) return st;

@@ -29,7 +29,7 @@ struct LayoutPlan {
   int32_t S;  // pairs per chunk (multiple of 64)
   int32_t C;  // chunks
   int32_t workgroups;  // ceil(C / kLayoutWaves)
-  size_t workspace_bytes;  // (E + 1) * C * 4: chunk histograms, expert-major, + bad-index row
+  size_t workspace_bytes;  // ceil(C/4)*4 * (E + 1) * 4: chunk histograms [C/4][E+1][4]
 };
 
 constexpr int kWave = 64;

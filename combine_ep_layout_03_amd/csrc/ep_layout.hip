@@ -22,12 +22,15 @@
 // Small problems (P <= kSmallMaxPairs, E <= kSmallMaxExperts, e.g. decode
 // batches) run all three phases in ONE launch of one 16-wave workgroup (its
 // waves are the chunks).  Larger ones use two launches: a count kernel writes
-// an expert-major [E+1][C] table of chunk histograms (row E counts bad
-// indices) to the workspace, and a scatter kernel in which every workgroup
-// reads that L2-resident table (16-byte loads, all in flight) to get the
-// totals and its own chunks' prefixes before walking.  (Measured at T*k =
-// 65536: making every workgroup of one launch count all pairs itself costs
-// more in LDS atomics than the second launch does.)
+// a [C/4][E+1][4] table of chunk histograms (a workgroup's 4 chunks are one
+// 16-byte group per expert; entry E counts bad indices) to the workspace,
+// and a scatter kernel in which every workgroup reads the whole table --
+// thread e takes expert e's groups, consecutive threads on consecutive 16
+// bytes, all loads in flight -- to get the totals and its own chunks'
+// prefixes before walking.  (Measured at T*k = 65536: reading expert-major
+// rows, each instruction touching 64 lines, cost 5.8 us of a 15 us scatter
+// kernel; making every workgroup of one launch count all pairs itself costs
+// more in LDS atomics than the second launch.)
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -64,7 +67,8 @@ LayoutPlan plan_layout(int64_t P, int E) {
   p.S = (int32_t)S;
   p.C = (int32_t)C;
   p.workgroups = (int32_t)((C + kLayoutWaves - 1) / kLayoutWaves);
-  p.workspace_bytes = (size_t)C * (size_t)(E + 1) * sizeof(int32_t);
+  // one 16-byte group of kLayoutWaves chunk counts per (workgroup, expert)
+  p.workspace_bytes = (size_t)p.workgroups * kLayoutWaves * (size_t)(E + 1) * sizeof(int32_t);
   return p;
 }
 
@@ -76,8 +80,8 @@ using dev::i32x4;
 using dev::wave_inclusive_scan;
 
 // Chunk histograms: wave c counts the pairs [c*S, c*S+S) in LDS and writes
-// column c of the expert-major table hist[E+1][C] (row E counts indices
-// outside [0,E)).
+// them to the table hist[C/4][E+1][4]: workgroup g's kLayoutWaves chunks form
+// one 16-byte group per expert (entry E counts indices outside [0,E)).
 __global__ __launch_bounds__(kThreads) void layout_count_kernel(const int32_t *__restrict__ idx,
                                                                  int64_t P, int32_t E, int32_t S,
                                                                  int32_t C,
@@ -117,8 +121,9 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(const int32_t *_
     }
   }
   __syncthreads();
-  if (c < C)
-    for (int e = lane; e < E1; e += kWave) hist[(int64_t)e * C + c] = h[e];
+  // every wave of the last workgroup writes, so chunks past C read as 0
+  int32_t *grp = hist + (int64_t)blockIdx.x * E1 * kLayoutWaves + wave;
+  for (int e = lane; e < E1; e += kWave) grp[(int64_t)e * kLayoutWaves] = h[e];
 }
 
 // Exclusive scan of a[0..n) in place, a[n] = total.  All NT threads of the
@@ -168,6 +173,8 @@ __device__ void write_handle(const int32_t *off, int32_t E, int32_t R, int32_t n
   }
 }
 
+constexpr int kTableBatch = 32;          // 16-byte table loads a scatter thread keeps in flight
+constexpr int kIlp = 4;                  // 64-pair steps whose ballot matches run interleaved
 constexpr int kStage = 16 * kWave;       // pairs a scatter-kernel wave stages in LDS at a time
 constexpr int kSmallStage = 8 * kWave;   // pairs a small-kernel wave stages (P <= 8192 -> <= 512)
 
@@ -177,9 +184,31 @@ constexpr int kSmallStage = 8 * kWave;   // pairs a small-kernel wave stages (P 
 // loads, one round trip), then ranks them 64 at a time in a rolled loop: the
 // layout runs few waves, each executing its code once, so compact loops
 // (warm instruction cache) beat unrolled straight-line code here.
+// Lane l's PL indices of the stage starting at pair qb (n pairs valid):
+// pairs qb + l*PL .. qb + l*PL + PL - 1, 16-byte loads where aligned.
+template <int PL>
+__device__ inline void load_stage(const int32_t *__restrict__ idx, int64_t qb, int64_t n, int lane,
+                                  i32x4 (&v)[PL / 4]) {
+  const int64_t pl = qb + (int64_t)lane * PL;
+  const bool vec = ((((uintptr_t)(idx + qb)) & 15u) == 0) && pl + PL <= qb + n;
+#pragma unroll
+  for (int u = 0; u < PL / 4; ++u) {
+    if (vec) {
+      v[u] = *reinterpret_cast<const i32x4 *>(idx + pl + 4 * u);
+    } else {
+      i32x4 t = {0, 0, 0, 0};
+      for (int i = 0; i < 4; ++i) t[i] = (pl + 4 * u + i < qb + n) ? idx[pl + 4 * u + i] : 0;
+      v[u] = t;
+    }
+  }
+}
+
+// `first`, if given, holds this lane's load_stage of the first stage (p0),
+// issued earlier by the caller so that its latency overlaps other work.
 template <int PL>
 __device__ void wave_walk(const int32_t *__restrict__ idx, int64_t p0, int64_t p1, int64_t P,
-                          int32_t E, int32_t *bw, int32_t *stage, const ep_layout_t &h) {
+                          int32_t E, int32_t *bw, int32_t *stage, const ep_layout_t &h,
+                          const i32x4 *first = nullptr) {
   static_assert(PL % 4 == 0, "whole 16-byte groups per lane");
   constexpr int kSt = PL * kWave;
   const int lane = threadIdx.x % kWave;
@@ -187,40 +216,51 @@ __device__ void wave_walk(const int32_t *__restrict__ idx, int64_t p0, int64_t p
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   for (int64_t qb = p0; qb < p1; qb += kSt) {
     const int64_t n = (p1 - qb < kSt) ? p1 - qb : kSt;
-    const int64_t pl = qb + (int64_t)lane * PL;
     i32x4 v[PL / 4];
-    const bool vec = ((((uintptr_t)(idx + qb)) & 15u) == 0) && pl + PL <= qb + n;
+    if (first && qb == p0) {
 #pragma unroll
-    for (int u = 0; u < PL / 4; ++u) {
-      if (vec) {
-        v[u] = *reinterpret_cast<const i32x4 *>(idx + pl + 4 * u);
-      } else {
-        i32x4 t = {0, 0, 0, 0};
-        for (int i = 0; i < 4; ++i) t[i] = (pl + 4 * u + i < qb + n) ? idx[pl + 4 * u + i] : 0;
-        v[u] = t;
-      }
+      for (int u = 0; u < PL / 4; ++u) v[u] = first[u];
+    } else {
+      load_stage<PL>(idx, qb, n, lane, v);
     }
 #pragma unroll
     for (int u = 0; u < PL / 4; ++u) *reinterpret_cast<i32x4 *>(stage + lane * PL + 4 * u) = v[u];
+    // kIlp steps of 64 pairs at a time: their match masks are independent
+    // (only the running bases carry from step to step), so their ballot
+    // chains are interleaved to hide each other's latency; the base updates
+    // then run in step order.
 #pragma unroll 1
-    for (int i = 0; i * kWave < n; ++i) {
-      const int64_t p = qb + i * kWave + lane;
-      const bool valid = i * kWave + lane < n;
-      const int32_t e = valid ? stage[i * kWave + lane] : 0;
-      // lanes whose expert matches this lane's in every bit: m &= (bit ? B : ~B)
-      uint64_t m = __ballot(valid);
-      for (int b = 0; b < nbits; ++b) {
-        const uint32_t bit = ((uint32_t)e >> b) & 1u;
-        const uint64_t bb = __ballot(bit != 0u);
-        const uint32_t flip = bit - 1u;  // 0 if the bit is set, all ones if not
-        m &= bb ^ (((uint64_t)flip << 32) | flip);
+    for (int i0 = 0; i0 * kWave < n; i0 += kIlp) {
+      int32_t e[kIlp];
+      bool valid[kIlp];
+      uint64_t m[kIlp];
+#pragma unroll
+      for (int s = 0; s < kIlp; ++s) {
+        const int i = (i0 + s) * kWave + lane;
+        valid[s] = i < n;
+        e[s] = valid[s] ? stage[i] : 0;
+        m[s] = __ballot(valid[s]);
       }
-      if (valid) {
-        const int32_t slot = bw[e] + __popcll(m & below);
-        h.slot_of[p] = slot;
-        if ((uint64_t)(uint32_t)slot < (uint64_t)P) h.src_of[slot] = (int32_t)p;
-        else atomicOr(h.error_flag, (int32_t)EP_DEVERR_INTERNAL);  // cannot happen; never write out of range
-        if ((m >> lane) == 1ull) bw[e] += __popcll(m);  // the group's highest lane
+      // lanes whose expert matches this lane's in every bit: m &= (bit ? B : ~B)
+      for (int b = 0; b < nbits; ++b) {
+#pragma unroll
+        for (int s = 0; s < kIlp; ++s) {
+          const uint32_t bit = ((uint32_t)e[s] >> b) & 1u;
+          const uint64_t bb = __ballot(bit != 0u);
+          const uint32_t flip = bit - 1u;  // 0 if the bit is set, all ones if not
+          m[s] &= bb ^ (((uint64_t)flip << 32) | flip);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < kIlp; ++s) {
+        if (valid[s]) {
+          const int64_t p = qb + (int64_t)(i0 + s) * kWave + lane;
+          const int32_t slot = bw[e[s]] + __popcll(m[s] & below);
+          h.slot_of[p] = slot;
+          if ((uint64_t)(uint32_t)slot < (uint64_t)P) h.src_of[slot] = (int32_t)p;
+          else atomicOr(h.error_flag, (int32_t)EP_DEVERR_INTERNAL);  // cannot happen; never write out of range
+          if ((m[s] >> lane) == 1ull) bw[e[s]] += __popcll(m[s]);  // the group's highest lane
+        }
       }
     }
   }
@@ -321,50 +361,53 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
   int32_t *stage = lds + ((E + 1) + kLayoutWaves * E + 8 + 3) / 4 * 4;  // [kLayoutWaves][kStage], 16-byte aligned
   const int tid = threadIdx.x, wave = tid / kWave;
   const int64_t c0 = (int64_t)blockIdx.x * kLayoutWaves;
+  // this wave's chunk, and its first stage of indices loaded now: the
+  // loads overlap the table reads below
+  const int64_t wc = c0 + wave;
+  const int64_t wp0 = wc * S;
+  const int64_t wp1 = (wp0 + S < P) ? wp0 + S : P;
+  i32x4 first[kStage / kWave / 4];
+  if (wc < C) {
+    const int64_t n0 = (wp1 - wp0 < kStage) ? wp1 - wp0 : kStage;
+    load_stage<kStage / kWave>(idx, wp0, n0, tid % kWave, first);
+  }
 
-  // Row e of the table holds expert e's count in every chunk: sum it for the
-  // total and, for this workgroup's chunks, the sums over the chunks before
-  // each of them (16-byte loads, 32 in flight per thread: one round trip for
-  // up to 128 chunks).
-  // c0 is a multiple of 4, so this workgroup's 4 chunks are one int4 group
-  const bool vec = (C % 4) == 0 && (((uintptr_t)hist) & 15u) == 0;
-  // Row E (indices outside [0,E)) is summed by all threads together, so no
-  // thread reads two rows when E is a multiple of the workgroup size.
-  // (the plan keeps C <= kThreads, so one element per thread; it is consumed
-  // only after the row loads below, so it adds no round trip)
-  int32_t badpart = (tid < C) ? hist[(int64_t)E * C + tid] : 0;
+  // Group q of the table holds the counts of chunks [4q, 4q+4) for every
+  // expert (and, at E, of bad indices).  Thread e reads the 16-byte groups of
+  // expert e: consecutive threads read consecutive groups, a batch of
+  // kTableBatch loads is in flight (one round trip for up to 4*kTableBatch
+  // chunks), the groups before this workgroup's give its prefix and its own
+  // group its chunks' counts.
+  const int64_t E1 = (int64_t)E + 1;
+  const int Q = (int)gridDim.x;  // groups = workgroups
+  const i32x4 *tab = reinterpret_cast<const i32x4 *>(hist);
+  int32_t badpart = 0;
+  if (tid < Q) {
+    const i32x4 b = tab[(int64_t)tid * E1 + E];
+    badpart = b[0] + b[1] + b[2] + b[3];
+  }
   for (int e = tid; e < E; e += kThreads) {
-    const int32_t *row = hist + (int64_t)e * C;
     int32_t run = 0, before = 0;
-    i32x4 mine = {0, 0, 0, 0};
+    const i32x4 mine = tab[(int64_t)blockIdx.x * E1 + e];
 #pragma unroll 1
-    for (int cb = 0; cb < C; cb += 128) {
-      i32x4 v[32];
+    for (int qb = 0; qb < Q; qb += kTableBatch) {
+      i32x4 v[kTableBatch];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const int c = cb + 4 * u;
-        if (vec && c + 4 <= C) {
-          v[u] = *reinterpret_cast<const i32x4 *>(row + c);
-        } else {
-          i32x4 t = {0, 0, 0, 0};
-          for (int i = 0; i < 4; ++i) t[i] = (c + i < C) ? row[c + i] : 0;
-          v[u] = t;
-        }
+      for (int u = 0; u < kTableBatch; ++u) {
+        const i32x4 z = {0, 0, 0, 0};
+        v[u] = (qb + u < Q) ? tab[(int64_t)(qb + u) * E1 + e] : z;
       }
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const int c = cb + 4 * u;
+      for (int u = 0; u < kTableBatch; ++u) {
         const int32_t s4 = v[u][0] + v[u][1] + v[u][2] + v[u][3];
         run += s4;
-        before += (c < c0) ? s4 : 0;
-        if (c == c0) mine = v[u];
+        before += (qb + u < (int)blockIdx.x) ? s4 : 0;
       }
     }
     int32_t pre[kLayoutWaves];
     pre[0] = before;
-    pre[1] = before + mine[0];
-    pre[2] = pre[1] + mine[1];
-    pre[3] = pre[2] + mine[2];
+#pragma unroll
+    for (int w = 1; w < kLayoutWaves; ++w) pre[w] = pre[w - 1] + mine[w - 1];
     off[e] = run;
 #pragma unroll
     for (int w = 0; w < kLayoutWaves; ++w) base[w * E + e] = pre[w];
@@ -382,11 +425,8 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
   for (int i = tid; i < kLayoutWaves * E; i += kThreads) base[i] += off[i % E];
   __syncthreads();
 
-  const int64_t c = c0 + wave;
-  if (c >= C) return;
-  const int64_t p0 = c * S;
-  const int64_t p1 = (p0 + S < P) ? p0 + S : P;
-  wave_walk<kStage / kWave>(idx, p0, p1, P, E, base + wave * E, stage + wave * kStage, h);
+  if (wc >= C) return;
+  wave_walk<kStage / kWave>(idx, wp0, wp1, P, E, base + wave * E, stage + wave * kStage, h, first);
 }
 
 }  // namespace

@@ -71,7 +71,7 @@ def test_capacity_and_workspace(lib):
     c = ep.Config(128, 7168, 8, 288, 36, fp8=True)
     assert ep.ep_layout_workspace_bytes(c) == 256
     c = ep.Config(30000, 7168, 8, 256, 8)  # 240000 pairs: chunks grow to 960 pairs so C <= 255
-    assert ep.ep_layout_workspace_bytes(c) == 250 * 257 * 4
+    assert ep.ep_layout_workspace_bytes(c) == 252 * 257 * 4  # 250 chunks in groups of 4
     # many pairs, many experts: the chunk count is capped so the table stays small
     c = ep.Config(1 << 20, 256, 8, 2048, 8)
     ws = ep.ep_layout_workspace_bytes(c)
@@ -107,6 +107,12 @@ def test_null_pointers_and_capacity_rejected_before_any_launch(lib):
     with pytest.raises(ep.EpError) as ei:
         ep.ep_layout(c, 8, h, None, 0)
     assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    for call in (lambda: ep.ep_layout(c, 8, h, 4100, 0),     # workspace not 16-byte aligned
+                 lambda: ep.ep_layout_dispatch(c, 8, h, 4100, 8, [8] * 4, None, 32, 0),
+                 lambda: ep.ep_route_layout(c, ep.Router(16), 8, None, None, None, 8, 8, h, 4100, 0)):
+        with pytest.raises(ep.EpError) as ei:
+            call()
+        assert ei.value.status == ep.EP_ERR_INVALID_ARG
     with pytest.raises(ep.EpError) as ei:
         ep.ep_dispatch(c, h, 8, 8, [8] * 4, None, 31, 0)
     assert ei.value.status == ep.EP_ERR_CAPACITY
