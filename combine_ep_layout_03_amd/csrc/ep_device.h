@@ -106,8 +106,13 @@ __device__ inline u32x4 quant_block16(u32x4 v0, u32x4 v1, float &s_out) {
   return u32x4{q0, q1, q2, q3};
 }
 
-// The same block quantization on 16 binary32 values per lane (8 lanes per
-// 128-element block): amax on |a| bit patterns, s = a/448, codes of a/s.
+// Block quantization of 16 binary32 activations per lane (8 lanes per
+// 128-element block) for the expert-side re-quantization, where the
+// activation itself is only specified to a tolerance: amax on |a| bit
+// patterns, s = a/448 (correctly rounded), codes of a * (1/s) -- one divide
+// per block instead of one per element, within 1.5 binary32 ulps of a/s, so a
+// code can differ from E4M3(a/s) only where a/s lies that close to an E4M3
+// rounding boundary.  Blocks so small that 1/s overflows divide exactly.
 __device__ inline u32x4 quant_block16_f32(const float *a, float &s_out) {
   uint32_t m = 0u;
 #pragma unroll
@@ -121,9 +126,21 @@ __device__ inline u32x4 quant_block16_f32(const float *a, float &s_out) {
   const bool zero = (m == 0u);
   const float s = zero ? 0.0f : __uint_as_float(m) / 448.0f;
   uint32_t w[4];
+  if (zero) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = zero ? 0u : e4m3_pack4(a[4 * i] / s, a[4 * i + 1] / s, a[4 * i + 2] / s, a[4 * i + 3] / s);
+    for (int i = 0; i < 4; ++i) w[i] = 0u;
+  } else {
+    const float inv = 1.0f / s;
+    if (inv <= 3.0e38f) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = e4m3_pack4(a[4 * i] * inv, a[4 * i + 1] * inv, a[4 * i + 2] * inv, a[4 * i + 3] * inv);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = e4m3_pack4(a[4 * i] / s, a[4 * i + 1] / s, a[4 * i + 2] / s, a[4 * i + 3] / s);
+    }
+  }
   s_out = s;
   return u32x4{w[0], w[1], w[2], w[3]};
 }

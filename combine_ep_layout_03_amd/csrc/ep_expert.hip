@@ -16,8 +16,9 @@
 // gate and up, computes a = g * rcp(1 + e^-g) * u in binary32 (the device
 // expf and the 1-ulp hardware reciprocal: the activation is specified to a
 // tolerance against a binary64 reference, and the correctly rounded divide
-// made this ALU-bound) and then the block amax / scale / codes exactly as
-// dispatch does (a correctly rounded a/s).
+// made this ALU-bound), then the block amax and the correctly rounded scale
+// as dispatch does, and codes of a * (1/s) with one divide per block (within
+// 1.5 binary32 ulps of a/s, inside the same tolerance).
 #include "ep_device.h"
 #include "ep_internal.h"
 

@@ -250,7 +250,9 @@ ep_status ep_combine_backward(const ep_config *cfg /*(host)*/, const ep_layout_t
  * the device): gate = act_in row [0, I), up = [I, 2I) (bf16);
  *   a = g * rcp(1 + expf(-g)) * u in fp32 (the device library's expf and
  *   the hardware reciprocal; a few fp32 ulps from the binary64 value), then
- *   per 128-element block s = a_max/448 and q = E4M3(a/s) as in ep_dispatch.
+ *   per 128-element block s = a_max/448 (correctly rounded) and
+ *   q = E4M3(a * (1/s)) (one divide per block; exact a/s for blocks whose
+ *   1/s overflows).
  * act_in: (host) R pointers to [capacity_rows, 2I] bf16; q_out: (host) R
  * pointers to [capacity_rows, I] bytes; scales_out: (host) R pointers to
  * [capacity_rows, I/128] fp32.  intermediate = I, a multiple of 128.  Rows
