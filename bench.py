@@ -134,7 +134,7 @@ KERNEL_KEYS = {
     "route": r"::route_kernel<\d+>\(",
     "layout_dispatch_small": r"::layout_dispatch_small_kernel<(true|false)>\(",
     "combine_shared": r"::combine_kernel<true>\(",
-    "combine_backward": r"::combine_backward_kernel\(",
+    "combine_backward": r"::combine_backward_(wave|wg)_kernel\(",
     "silu_mul_quant": r"::silu_mul_quant_kernel\(",
 }
 CAL_COPY_KEY = "bitwise_not"      # elementwise kernel: reads and writes CAL_BYTES

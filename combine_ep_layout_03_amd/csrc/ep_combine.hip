@@ -142,13 +142,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 }
 
 // Backward of combine ([DeepEP overview], "Pola penggunaan ...": the backward
-// of combine is a dispatch).  One wave per token (grid-stride); the k pairs
+// of combine is a dispatch), for large batches.  One wave per token
+// (grid-stride); the k pairs
 // are taken in blocks of 8: for each block the wave streams the token's
 // grad_out row once, writes bf16(RN32(w_j * g)) into each pair's gradient row
 // and, when y is given, accumulates each pair's dot product <g, y_j> per lane
 // (fp32 fma over the lane's channels in order), then reduces it across the
 // wave with a fixed xor-butterfly, so the result is deterministic.
-__global__ __launch_bounds__(kThreads) void combine_backward_kernel(
+__global__ __launch_bounds__(kThreads) void combine_backward_wave_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ slot_of,
     const int32_t *__restrict__ rank_offsets, int32_t *__restrict__ err,
     const uint16_t *__restrict__ gout, const float *__restrict__ w, int32_t T, int32_t H,
@@ -229,6 +230,114 @@ __global__ __launch_bounds__(kThreads) void combine_backward_kernel(
   }
 }
 
+// The same for small batches (T < kBwdWgMaxTokens, e.g. decode), where one
+// wave per token leaves the GPU nearly idle.  One workgroup of kBwdWaves waves per token
+// (grid-stride), its threads splitting the row's 16-byte chunks; the k pairs
+// are taken in blocks of 8: for each block the workgroup streams the token's
+// grad_out row once, writes bf16(RN32(w_j * g)) into each pair's gradient row
+// and, when y is given, accumulates each pair's dot product <g, y_j> per
+// thread (fp32 fma over its channels in order), reduces it across each wave
+// with a fixed xor-butterfly and then over the waves in ascending order, so
+// the result is deterministic and needs no scratch memory.  (Measured on
+// MI355X: at 128 tokens 16 us against 50 us for one wave per token; at 8192
+// tokens 411 us against 387 us, hence the split.)
+constexpr int kBwdWaves = 8;
+constexpr int32_t kBwdWgMaxTokens = 2048;
+constexpr int kBwdThreads = kBwdWaves * kWave;
+
+__global__ __launch_bounds__(kBwdThreads) void combine_backward_wg_kernel(
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ slot_of,
+    const int32_t *__restrict__ rank_offsets, int32_t *__restrict__ err,
+    const uint16_t *__restrict__ gout, const float *__restrict__ w, int32_t T, int32_t H,
+    int32_t k, int32_t E, int32_t El, int64_t cap, RankCPtrs ry, RankPtrs rg,
+    float *__restrict__ gw) {
+  __shared__ float part[kBwdWaves][EP_MAX_TOPK];  // per-wave dot products
+  if (*err != 0) return;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int nch = H / 8;
+  const bool want_w = gw != nullptr;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    // every wave resolves the token's rows itself (L2 hits), so all waves
+    // agree on skipping a bad token without a barrier
+    uint64_t dst = 0, src = 0;
+    float wj = 0.0f;
+    if (lane < k) {
+      const int64_t p = t * k + lane;
+      const int32_t e = idx[p];
+      if ((uint32_t)e < (uint32_t)E) {
+        const int32_t r = e / El;
+        const int64_t rr = (int64_t)slot_of[p] - rank_offsets[r];
+        if (rr >= 0 && rr < cap) {
+          dst = (uint64_t)rg.p[r] + (uint64_t)(rr * (int64_t)H * 2);
+          if (want_w) src = (uint64_t)ry.p[r] + (uint64_t)(rr * (int64_t)H * 2);
+        }
+      }
+      if (dst == 0 && wave == 0) atomicOr(err, (int32_t)EP_DEVERR_ROW);
+      wj = w ? w[p] : 1.0f;
+    }
+    if (__ballot(lane < k && dst == 0) != 0) continue;  // a bad row: write nothing for t
+    const u32x4 *grow = reinterpret_cast<const u32x4 *>(gout + t * H);
+    for (int j0 = 0; j0 < k; j0 += kJB) {
+      float acc[kJB];
+#pragma unroll
+      for (int jj = 0; jj < kJB; ++jj) acc[jj] = 0.0f;
+      for (int c = tid; c < nch; c += kBwdThreads) {
+        const u32x4 g = __builtin_nontemporal_load(grow + c);
+        u32x4 v[kJB];
+        if (want_w) {
+#pragma unroll
+          for (int jj = 0; jj < kJB; ++jj)
+            if (j0 + jj < k)
+              v[jj] = __builtin_nontemporal_load(
+                  reinterpret_cast<const u32x4 *>(readlane64(src, j0 + jj)) + c);
+        }
+#pragma unroll
+        for (int jj = 0; jj < kJB; ++jj) {
+          if (j0 + jj < k) {
+            const float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j0 + jj));
+            float prod[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              prod[2 * i] = wv * __uint_as_float(g[i] << 16);
+              prod[2 * i + 1] = wv * __uint_as_float(g[i] & 0xFFFF0000u);
+            }
+            u32x4 *drow = reinterpret_cast<u32x4 *>(readlane64(dst, j0 + jj));
+            __builtin_nontemporal_store(pack8(prod), drow + c);
+            if (want_w) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                acc[jj] = __builtin_fmaf(__uint_as_float(g[i] << 16),
+                                         __uint_as_float(v[jj][i] << 16), acc[jj]);
+                acc[jj] = __builtin_fmaf(__uint_as_float(g[i] & 0xFFFF0000u),
+                                         __uint_as_float(v[jj][i] & 0xFFFF0000u), acc[jj]);
+              }
+            }
+          }
+        }
+      }
+      if (want_w) {
+#pragma unroll
+        for (int jj = 0; jj < kJB; ++jj) {
+          float a = acc[jj];
+#pragma unroll
+          for (int o = kWave / 2; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+          if (lane == 0 && j0 + jj < k) part[wave][j0 + jj] = a;
+        }
+      }
+    }
+    if (want_w) {
+      __syncthreads();
+      if (tid < k) {
+        float a = 0.0f;
+#pragma unroll
+        for (int wv = 0; wv < kBwdWaves; ++wv) a += part[wv][tid];
+        gw[t * k + tid] = a;
+      }
+      __syncthreads();  // part is reused for the next token
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void unpermute_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ slot_of,
     const int32_t *__restrict__ rank_offsets, int32_t *__restrict__ err, int64_t P, int32_t H,
@@ -273,12 +382,22 @@ hipError_t launch_combine_backward(const ep_config &c, const ep_layout_t &h,
                                    const int32_t *topk_idx, const void *grad_out, const float *w,
                                    const RankCPtrs &ry, const RankPtrs &rg, float *grad_w,
                                    int64_t capacity_rows, hipStream_t s) {
-  const int grid = row_grid(c, c.num_tokens);
-  hipLaunchKernelGGL(combine_backward_kernel, dim3(grid), dim3(kThreads), 0, s, topk_idx,
-                     h.slot_of, h.rank_offsets, h.error_flag,
-                     static_cast<const uint16_t *>(grad_out), w, c.num_tokens, c.hidden,
-                     c.num_topk, c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,
-                     rg, grad_w);
+  // the path depends on T only, so results never depend on num_workgroups
+  if (c.num_tokens < kBwdWgMaxTokens) {
+    const int grid = c.num_workgroups > 0 ? c.num_workgroups : c.num_tokens;
+    hipLaunchKernelGGL(combine_backward_wg_kernel, dim3(grid), dim3(kBwdThreads), 0, s, topk_idx,
+                       h.slot_of, h.rank_offsets, h.error_flag,
+                       static_cast<const uint16_t *>(grad_out), w, c.num_tokens, c.hidden,
+                       c.num_topk, c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,
+                       rg, grad_w);
+  } else {
+    const int grid = row_grid(c, c.num_tokens);
+    hipLaunchKernelGGL(combine_backward_wave_kernel, dim3(grid), dim3(kThreads), 0, s, topk_idx,
+                       h.slot_of, h.rank_offsets, h.error_flag,
+                       static_cast<const uint16_t *>(grad_out), w, c.num_tokens, c.hidden,
+                       c.num_topk, c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,
+                       rg, grad_w);
+  }
   return hipGetLastError();
 }
 

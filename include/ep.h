@@ -230,8 +230,10 @@ ep_status ep_combine_shared(const ep_config *cfg /*(host)*/, const ep_layout_t *
  *   grad_recv[r] row `row` (H bf16) := bf16(w[t][j] * grad_out[t][h]), the
  *     product one fp32 multiply, rounded to nearest even (topk_weights NULL:
  *     unit weights, an exact copy);
- *   grad_weights[t][j] := <grad_out[t], y row>, accumulated in fp32 (each
- *     lane's channels in order, then a fixed butterfly across the wave), when
+ *   grad_weights[t][j] := <grad_out[t], y row>, accumulated in fp32 in a
+ *     fixed order (each thread's channels in order, a butterfly across the
+ *     wave and, for T < 2048, where a token takes a workgroup of 8 waves,
+ *     those waves in order), so it does not depend on num_workgroups, when
  *     recv_y / grad_weights are given; pass both or neither.
  * The backward of dispatch is ep_combine with topk_weights NULL applied to
  * the gradient rows.  grad_out is [T,H] bf16; grad_recv and recv_y are (host)
