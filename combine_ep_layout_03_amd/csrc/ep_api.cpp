@@ -39,12 +39,35 @@ bool workspace_ok(const void *ws) { return ws && ((uintptr_t)ws & 15u) == 0; }
 
 ep_status from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
 
-void trace(const char *what, const ep_config *c, int grid) {
+// EP_DEBUG=1: one line per call on stderr.
+void trace(const char *what, const ep_config *c) {
   if (!debug_enabled()) return;
-  std::fprintf(stderr,
-               "[ep] %s T=%d H=%d k=%d E=%d R=%d dtype=%d grid=%d block=%d\n", what,
+  std::fprintf(stderr, "[ep] %s T=%d H=%d k=%d E=%d R=%d dtype=%d num_workgroups=%d\n", what,
                c->num_tokens, c->hidden, c->num_topk, c->num_experts, c->num_ranks,
-               c->dispatch_dtype, grid, ep::kRowWaves * ep::kWave);
+               c->dispatch_dtype, c->num_workgroups);
+}
+
+// The R receive (and, for FP8, scale) buffers of a dispatch; false if one is NULL.
+bool recv_ptrs(const ep_config *cfg, void *const *recv_x, float *const *recv_scales,
+               ep::RankPtrs &rx, ep::ScalePtrs &rs) {
+  const bool fp8 = cfg->dispatch_dtype == EP_DTYPE_FP8_E4M3;
+  if (!recv_x || (fp8 && !recv_scales)) return false;
+  for (int r = 0; r < cfg->num_ranks; ++r) {
+    if (!recv_x[r] || (fp8 && !recv_scales[r])) return false;
+    rx.p[r] = recv_x[r];
+    rs.p[r] = fp8 ? recv_scales[r] : nullptr;
+  }
+  return true;
+}
+
+// R read-only row buffers; false if the array or one pointer is NULL.
+bool const_ptrs(const ep_config *cfg, const void *const *bufs, ep::RankCPtrs &out) {
+  if (!bufs) return false;
+  for (int r = 0; r < cfg->num_ranks; ++r) {
+    if (!bufs[r]) return false;
+    out.p[r] = bufs[r];
+  }
+  return true;
 }
 
 // Shared checks of dispatch / combine / unpermute.
@@ -123,20 +146,10 @@ ep_status ep_dispatch(const ep_config *cfg, const ep_layout_t *h, const int32_t 
                       int64_t capacity_rows, hipStream_t stream) {
   ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
   if (st != EP_OK) return st;
-  if (!x || !recv_x) return EP_ERR_INVALID_ARG;
-  const bool fp8 = cfg->dispatch_dtype == EP_DTYPE_FP8_E4M3;
-  if (fp8 && !recv_scales) return EP_ERR_INVALID_ARG;
   ep::RankPtrs rx{};
   ep::ScalePtrs rs{};
-  for (int r = 0; r < cfg->num_ranks; ++r) {
-    if (!recv_x[r]) return EP_ERR_INVALID_ARG;
-    rx.p[r] = recv_x[r];
-    if (fp8) {
-      if (!recv_scales[r]) return EP_ERR_INVALID_ARG;
-      rs.p[r] = recv_scales[r];
-    }
-  }
-  trace("dispatch", cfg, ep::row_grid(*cfg, cfg->num_tokens));
+  if (!x || !recv_ptrs(cfg, recv_x, recv_scales, rx, rs)) return EP_ERR_INVALID_ARG;
+  trace("dispatch", cfg);
   return from_hip(ep::launch_dispatch(*cfg, *h, topk_idx, x, rx, rs, capacity_rows, stream));
 }
 
@@ -148,21 +161,11 @@ ep_status ep_layout_dispatch(const ep_config *cfg, const int32_t *topk_idx, cons
     return EP_ERR_INVALID_ARG;
   ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
   if (st != EP_OK) return st;
-  if (!x || !recv_x) return EP_ERR_INVALID_ARG;
-  const bool fp8 = cfg->dispatch_dtype == EP_DTYPE_FP8_E4M3;
-  if (fp8 && !recv_scales) return EP_ERR_INVALID_ARG;
   ep::RankPtrs rx{};
   ep::ScalePtrs rs{};
-  for (int r = 0; r < cfg->num_ranks; ++r) {
-    if (!recv_x[r]) return EP_ERR_INVALID_ARG;
-    rx.p[r] = recv_x[r];
-    if (fp8) {
-      if (!recv_scales[r]) return EP_ERR_INVALID_ARG;
-      rs.p[r] = recv_scales[r];
-    }
-  }
+  if (!x || !recv_ptrs(cfg, recv_x, recv_scales, rx, rs)) return EP_ERR_INVALID_ARG;
   if (ep::fused_layout_dispatch_ok(*cfg)) {
-    trace("layout_dispatch (one launch)", cfg, 0);
+    trace("layout_dispatch (one launch)", cfg);
     return from_hip(
         ep::launch_layout_dispatch_small(*cfg, topk_idx, *h, x, rx, rs, capacity_rows, stream));
   }
@@ -170,7 +173,7 @@ ep_status ep_layout_dispatch(const ep_config *cfg, const int32_t *topk_idx, cons
       ep::plan_layout((int64_t)cfg->num_tokens * cfg->num_topk, cfg->num_experts);
   hipError_t e = ep::launch_layout(*cfg, plan, topk_idx, *h, workspace, stream);
   if (e != hipSuccess) return EP_ERR_HIP;
-  trace("layout_dispatch (layout, then dispatch)", cfg, ep::row_grid(*cfg, cfg->num_tokens));
+  trace("layout_dispatch (layout, then dispatch)", cfg);
   return from_hip(ep::launch_dispatch(*cfg, *h, topk_idx, x, rx, rs, capacity_rows, stream));
 }
 
@@ -179,13 +182,9 @@ ep_status ep_combine(const ep_config *cfg, const ep_layout_t *h, const int32_t *
                      int64_t capacity_rows, hipStream_t stream) {
   ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
   if (st != EP_OK) return st;
-  if (!recv_y || !out) return EP_ERR_INVALID_ARG;
   ep::RankCPtrs ry{};
-  for (int r = 0; r < cfg->num_ranks; ++r) {
-    if (!recv_y[r]) return EP_ERR_INVALID_ARG;
-    ry.p[r] = recv_y[r];
-  }
-  trace("combine", cfg, ep::row_grid(*cfg, cfg->num_tokens));
+  if (!out || !const_ptrs(cfg, recv_y, ry)) return EP_ERR_INVALID_ARG;
+  trace("combine", cfg);
   return from_hip(ep::launch_combine(*cfg, *h, topk_idx, ry, topk_weights, nullptr, out,
                                      capacity_rows, stream));
 }
@@ -196,13 +195,9 @@ ep_status ep_combine_shared(const ep_config *cfg, const ep_layout_t *h, const in
                             hipStream_t stream) {
   ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
   if (st != EP_OK) return st;
-  if (!recv_y || !out || !shared) return EP_ERR_INVALID_ARG;
   ep::RankCPtrs ry{};
-  for (int r = 0; r < cfg->num_ranks; ++r) {
-    if (!recv_y[r]) return EP_ERR_INVALID_ARG;
-    ry.p[r] = recv_y[r];
-  }
-  trace("combine_shared", cfg, ep::row_grid(*cfg, cfg->num_tokens));
+  if (!out || !shared || !const_ptrs(cfg, recv_y, ry)) return EP_ERR_INVALID_ARG;
+  trace("combine_shared", cfg);
   return from_hip(ep::launch_combine(*cfg, *h, topk_idx, ry, topk_weights, shared, out,
                                      capacity_rows, stream));
 }
@@ -217,15 +212,12 @@ ep_status ep_combine_backward(const ep_config *cfg, const ep_layout_t *h, const 
   if ((recv_y == nullptr) != (grad_weights == nullptr)) return EP_ERR_INVALID_ARG;
   ep::RankCPtrs ry{};
   ep::RankPtrs rg{};
+  if (recv_y && !const_ptrs(cfg, recv_y, ry)) return EP_ERR_INVALID_ARG;
   for (int r = 0; r < cfg->num_ranks; ++r) {
     if (!grad_recv[r]) return EP_ERR_INVALID_ARG;
     rg.p[r] = grad_recv[r];
-    if (recv_y) {
-      if (!recv_y[r]) return EP_ERR_INVALID_ARG;
-      ry.p[r] = recv_y[r];
-    }
   }
-  trace("combine_backward", cfg, ep::row_grid(*cfg, cfg->num_tokens));
+  trace("combine_backward", cfg);
   return from_hip(ep::launch_combine_backward(*cfg, *h, topk_idx, grad_out, topk_weights, ry, rg,
                                               grad_weights, capacity_rows, stream));
 }
@@ -247,7 +239,7 @@ ep_status ep_silu_mul_quant(const ep_config *cfg, const ep_layout_t *h, int32_t 
     q.p[r] = q_out[r];
     s.p[r] = scales_out[r];
   }
-  trace("silu_mul_quant", cfg, 0);
+  trace("silu_mul_quant", cfg);
   return from_hip(ep::launch_silu_mul_quant(*cfg, *h, intermediate, in, q, s, capacity_rows,
                                             stream));
 }
@@ -257,13 +249,9 @@ ep_status ep_unpermute(const ep_config *cfg, const ep_layout_t *h, const int32_t
                        hipStream_t stream) {
   ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
   if (st != EP_OK) return st;
-  if (!recv_y || !out) return EP_ERR_INVALID_ARG;
   ep::RankCPtrs ry{};
-  for (int r = 0; r < cfg->num_ranks; ++r) {
-    if (!recv_y[r]) return EP_ERR_INVALID_ARG;
-    ry.p[r] = recv_y[r];
-  }
-  trace("unpermute", cfg, ep::row_grid(*cfg, (int64_t)cfg->num_tokens * cfg->num_topk));
+  if (!out || !const_ptrs(cfg, recv_y, ry)) return EP_ERR_INVALID_ARG;
+  trace("unpermute", cfg);
   return from_hip(ep::launch_unpermute(*cfg, *h, topk_idx, ry, out, capacity_rows, stream));
 }
 
@@ -274,7 +262,7 @@ ep_status ep_route(const ep_config *cfg, const ep_router_t *router, const float 
   const ep_status st = route_call_ok(cfg, router, logits, replica_offsets, replica_slots,
                                      topk_idx, topk_weights);
   if (st != EP_OK) return st;
-  trace("route", cfg, ep::row_grid(*cfg, cfg->num_tokens));
+  trace("route", cfg);
   return from_hip(ep::launch_route(*cfg, *router, logits, bias, replica_offsets, replica_slots,
                                    topk_idx, topk_weights, stream));
 }

@@ -71,7 +71,6 @@ hipError_t launch_layout_dispatch_small(const ep_config &c, const int32_t *topk_
                                         const ep_layout_t &h, const void *x, const RankPtrs &rx,
                                         const ScalePtrs &rs, int64_t capacity_rows, hipStream_t s);
 
-size_t route_lds_bytes(int32_t El, int32_t gate);
 hipError_t launch_route(const ep_config &c, const ep_router_t &rt, const float *logits,
                         const float *bias, const int32_t *rep_off, const int32_t *rep_slots,
                         int32_t *topk_idx, float *topk_w, hipStream_t s);

@@ -299,16 +299,11 @@ __global__ __launch_bounds__(kWave) void route_kernel(
 
 }  // namespace
 
-size_t route_lds_bytes(int32_t El, int32_t gate) {
-  (void)gate;
-  return (size_t)El * sizeof(float);
-}
-
 hipError_t launch_route(const ep_config &c, const ep_router_t &rt, const float *logits,
                         const float *bias, const int32_t *rep_off, const int32_t *rep_slots,
                         int32_t *topk_idx, float *topk_w, hipStream_t s) {
   const int grid = row_grid(c, c.num_tokens);
-  const size_t lds = route_lds_bytes(rt.num_logical, rt.gate);
+  const size_t lds = (size_t)rt.num_logical * sizeof(float);  // scores, for the LDS group path
 #define EP_ROUTE_LAUNCH(N)                                                                     \
   hipLaunchKernelGGL(route_kernel<N>, dim3(grid), dim3(kWave), lds, s, logits, bias, rep_off, \
                      rep_slots, c.num_tokens, rt.num_logical, c.num_topk, rt.gate,            \

@@ -118,6 +118,14 @@ def rel_err(g_bits: np.ndarray, r_bits: np.ndarray) -> float:
     return float(np.max(np.abs(g - r) / np.maximum(np.abs(r), 1e-3))) if g.size else 0.0
 
 
+def norm_err(g_bits: np.ndarray, r_bits: np.ndarray) -> float:
+    """Normwise error max|g - r| / max|r| over bf16 outputs (reported beside
+    the elementwise bar)."""
+    g = (g_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    r = (r_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return float(np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-30)) if g.size else 0.0
+
+
 def rows_to_dev(cap, H, rows_np):
     """R capacity-sized bf16 device buffers holding the given valid rows."""
     bufs = []

@@ -19,7 +19,7 @@ import combine_ep_layout_03_amd as ep
 import oracle
 from workloads import CONFIGS, Workload, make_workload, make_expert_rows, edge_case_x, bf16_from_f32
 
-from gpu_util import GpuRun, POISON, rel_err, say, u16, to_dev
+from gpu_util import GpuRun, POISON, norm_err, rel_err, say, u16, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -241,7 +241,8 @@ def check_combine(w, run, L, ys, weights=True):
     got = u16(run.out)
     err = rel_err(got, ref)
     mism = int(np.count_nonzero(got != ref))
-    say(f"  combine {w.name}: max rel err {err:.3g}, bit mismatches {mism} / {got.size}")
+    say(f"  combine {w.name}: max rel err {err:.3g}, normwise {norm_err(got, ref):.3g}, "
+        f"bit mismatches {mism} / {got.size}")
     assert err <= 1e-2
     return mism
 
