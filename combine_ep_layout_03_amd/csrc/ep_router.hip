@@ -297,11 +297,237 @@ __global__ __launch_bounds__(kWave) void route_kernel(
   }
 }
 
+// ---- four tokens per wave ------------------------------------------------
+// For T >= kRowMinTokens, El <= 512, k <= 16 and groups covering power-of-two
+// runs of at most 16 lanes, each 16-lane row of the wave routes its own token: the same four DPP
+// steps then leave every lane of a row holding that row's maximum or sum (no
+// readlanes), one ballot serves the four tokens' picks, and the winner's
+// local index comes over with one shuffle, so the serial pick chain is shared
+// by four tokens.  Results are those of route_kernel bit for bit (same
+// binary32 scores, same tie rule: the lowest lane of a row holds the lowest
+// id; renormalization sums the picks in order).
+constexpr int kRowLanes = 16;
+constexpr int kRowTokens = kWave / kRowLanes;
+// Below this many tokens the one-token kernel is faster: with four tokens a
+// wave each lane evaluates four times the gates in sequence, and a small
+// batch has too few waves to hide that (measured on MI355X: 128 tokens x 256
+// experts 7.1 us one-token, 12.0 us four-token; 8192 tokens 16.1 / 14.4 us).
+constexpr int32_t kRowMinTokens = 2048;
+
+__device__ inline uint32_t row_max_u32(uint32_t v) {
+  v = umax(v, dpp<kDppXor1>(v));
+  v = umax(v, dpp<kDppXor2>(v));
+  v = umax(v, dpp<kDppHalfMirror>(v));
+  return umax(v, dpp<kDppMirror>(v));
+}
+
+__device__ inline float row_max_f32(float v) {
+  v = fmaxf(v, __uint_as_float(dpp<kDppXor1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kDppXor2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kDppHalfMirror>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(dpp<kDppMirror>(__float_as_uint(v))));
+}
+
+__device__ inline double row_sum_f64(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  return v + dpp_f64<kDppMirror>(v);
+}
+
+// Winner of each row among its offering lanes: the largest bits, then the
+// lowest lane; the winner's index within the row, or -1 if none offers.
+__device__ inline int row_pick(bool has, uint32_t bits, int row, uint32_t &best_bits) {
+  const uint32_t mx = row_max_u32(has ? bits : 0u);
+  const uint64_t b = __ballot(has && bits == mx);
+  const uint32_t m = (uint32_t)(b >> (row * kRowLanes)) & 0xFFFFu;
+  best_bits = mx;
+  return m ? (int)__builtin_ctz(m) : -1;
+}
+
+template <int NPER>
+__global__ __launch_bounds__(kWave) void route_rows_kernel(
+    const float *__restrict__ logits, const float *__restrict__ bias,
+    const int32_t *__restrict__ rep_off, const int32_t *__restrict__ rep_slots, int32_t T,
+    int32_t El, int32_t k, int32_t gate, int32_t G, int32_t TG, int32_t topn, int32_t renorm,
+    int32_t *__restrict__ idx, float *__restrict__ wout) {
+  const int lane = threadIdx.x, row = lane / kRowLanes, lr = lane % kRowLanes;
+  const int e0 = lr * NPER;
+  const int gs = El / G;
+  const int lpg = gs / NPER;  // lanes per group (G > 1: a power of two <= 16)
+  const bool vec = NPER >= 4 && (El & 3) == 0 && (((uintptr_t)logits) & 15u) == 0 &&
+                   (!bias || (((uintptr_t)bias) & 15u) == 0);
+  uint32_t valid_e = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) valid_e |= (e0 + i < El) ? 1u << i : 0u;
+
+  for (int64_t tb = (int64_t)blockIdx.x * kRowTokens; tb < T;
+       tb += (int64_t)gridDim.x * kRowTokens) {
+    const int64_t t = tb + row;
+    const bool live = t < T;
+    const uint32_t valid = live ? valid_e : 0u;
+    const float *zr = logits + (live ? t : 0) * (int64_t)El;
+    float z[NPER];
+    if (vec) {
+#pragma unroll
+      for (int i = 0; i < NPER; i += 4) {
+        float4 v = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+        if ((valid >> i) & 1u) {
+          v = *reinterpret_cast<const float4 *>(zr + e0 + i);
+          if (bias) b = *reinterpret_cast<const float4 *>(bias + e0 + i);
+        }
+        z[i] = bias ? v.x + b.x : v.x;
+        z[i + 1] = bias ? v.y + b.y : v.y;
+        z[i + 2] = bias ? v.z + b.z : v.z;
+        z[i + 3] = bias ? v.w + b.w : v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        const int e = e0 + i;
+        z[i] = ((valid >> i) & 1u) ? (bias ? zr[e] + bias[e] : zr[e]) : 0.0f;
+      }
+    }
+
+    float s[NPER];
+    if (gate == EP_GATE_SOFTMAX) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        if ((valid >> i) & 1u) m = fmaxf(m, z[i]);
+      m = row_max_f32(m);
+      double ex[NPER];
+      double sum = 0.0;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        ex[i] = ((valid >> i) & 1u) ? exp((double)z[i] - (double)m) : 0.0;
+        sum += ex[i];
+      }
+      sum = row_sum_f64(sum);
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) s[i] = (float)(ex[i] / sum);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) s[i] = (float)(1.0 / (1.0 + exp(-(double)z[i])));
+    }
+
+    uint32_t elig = valid;
+    if (G > 1) {
+      uint32_t a1 = 0, a2 = 0;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        const uint32_t b = __float_as_uint(s[i]);
+        if ((valid >> i) & 1u) {
+          a2 = umax(a2, umin(a1, b));
+          a1 = umax(a1, b);
+        }
+      }
+      for (int off = 1; off < lpg; off <<= 1) {
+        const uint32_t b1 = xor_lane(a1, off), b2 = xor_lane(a2, off);
+        a2 = umax(umin(a1, b1), umax(a2, b2));
+        a1 = umax(a1, b1);
+      }
+      const int grp = lr / lpg;
+      const float g = (topn == 1 || gs == 1) ? __uint_as_float(a1)
+                                             : __uint_as_float(a1) + __uint_as_float(a2);
+      bool offer = live && (lr % lpg) == 0 && grp < G;
+      uint32_t kept = 0;
+      for (int r = 0; r < TG; ++r) {
+        uint32_t bb;
+        const int wl = row_pick(offer, __float_as_uint(g), row, bb);
+        if (wl >= 0) {
+          kept |= 1u << (wl / lpg);
+          if (lr == wl) offer = false;
+        }
+      }
+      elig = ((kept >> grp) & 1u) ? valid : 0u;
+    }
+
+    int ci = -1;
+    uint32_t cb = 0;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const uint32_t b = __float_as_uint(s[i]);
+      if (((elig >> i) & 1u) && (ci < 0 || b > cb)) {
+        ci = i;
+        cb = b;
+      }
+    }
+    int32_t sel = -1;
+    float ws = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      uint32_t bb;
+      const int wl = row_pick(ci >= 0, cb, row, bb);
+      const int ciw = __shfl(ci, row * kRowLanes + (wl < 0 ? 0 : wl), kWave);
+      if (wl >= 0) {
+        if (lr == j) {
+          sel = wl * NPER + ciw;
+          ws = __uint_as_float(bb);
+        }
+        if (lr == wl) {
+          elig &= ~(1u << ci);
+          ci = -1;
+          cb = 0;
+#pragma unroll
+          for (int i = 0; i < NPER; ++i) {
+            const uint32_t b = __float_as_uint(s[i]);
+            if (((elig >> i) & 1u) && (ci < 0 || b > cb)) {
+              ci = i;
+              cb = b;
+            }
+          }
+        }
+      }
+    }
+
+    if (renorm) {
+      float sum = 0.0f;
+      for (int j = 0; j < k; ++j) sum += __shfl(ws, row * kRowLanes + j, kWave);
+      if (sum > 0.0f) ws = ws / sum;
+    }
+    if (live && lr < k) {
+      int32_t phys = sel;
+      if (rep_off && sel >= 0) {
+        const int32_t n = rep_off[sel + 1] - rep_off[sel];
+        phys = n > 0 ? rep_slots[rep_off[sel] + (int32_t)(t % n)] : -1;
+      }
+      idx[t * k + lr] = phys;
+      wout[t * k + lr] = ws;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_route(const ep_config &c, const ep_router_t &rt, const float *logits,
                         const float *bias, const int32_t *rep_off, const int32_t *rep_slots,
                         int32_t *topk_idx, float *topk_w, hipStream_t s) {
+  const int El = rt.num_logical;
+  // four tokens per wave where the shape allows it
+  int nrow = 1;
+  while (nrow * kRowLanes < El) nrow *= 2;
+  const int gs = El / rt.num_groups, lpg = gs / nrow;
+  const bool rows = c.num_tokens >= kRowMinTokens && El <= kRowLanes * 32 &&
+                    c.num_topk <= kRowLanes &&
+                    (rt.num_groups == 1 ||
+                     (gs % nrow == 0 && lpg <= kRowLanes && (lpg & (lpg - 1)) == 0));
+  if (rows) {
+    const int grid = row_grid(c, (c.num_tokens + kRowTokens - 1) / kRowTokens);
+#define EP_ROUTE_ROWS(N)                                                                         \
+  hipLaunchKernelGGL(route_rows_kernel<N>, dim3(grid), dim3(kWave), 0, s, logits, bias, rep_off, \
+                     rep_slots, c.num_tokens, El, c.num_topk, rt.gate, rt.num_groups,          \
+                     rt.topk_groups, rt.group_topn, rt.renormalize, topk_idx, topk_w)
+    switch (nrow) {
+      case 1: EP_ROUTE_ROWS(1); break;
+      case 2: EP_ROUTE_ROWS(2); break;
+      case 4: EP_ROUTE_ROWS(4); break;
+      case 8: EP_ROUTE_ROWS(8); break;
+      case 16: EP_ROUTE_ROWS(16); break;
+      default: EP_ROUTE_ROWS(32); break;
+    }
+#undef EP_ROUTE_ROWS
+    return hipGetLastError();
+  }
   const int grid = row_grid(c, c.num_tokens);
   const size_t lds = (size_t)rt.num_logical * sizeof(float);  // scores, for the LDS group path
 #define EP_ROUTE_LAUNCH(N)                                                                     \
@@ -309,7 +535,6 @@ hipError_t launch_route(const ep_config &c, const ep_router_t &rt, const float *
                      rep_slots, c.num_tokens, rt.num_logical, c.num_topk, rt.gate,            \
                      rt.num_groups, rt.topk_groups, rt.group_topn, rt.renormalize, topk_idx,  \
                      topk_w)
-  const int El = rt.num_logical;
   if (El <= 64) EP_ROUTE_LAUNCH(1);
   else if (El <= 128) EP_ROUTE_LAUNCH(2);
   else if (El <= 256) EP_ROUTE_LAUNCH(4);

@@ -121,6 +121,40 @@ def test_route_bias_and_replicas():
           rep_slots=slots)
 
 
+# Batches of at least 2048 tokens take the four-tokens-per-wave kernel when
+# El <= 512, k <= 16 and the groups cover power-of-two runs of <= 16 lanes
+# (16-lane rows, each lane holding the next power of two >= El/16 experts);
+# other shapes fall back to the one-token kernel.  T = 2101 leaves a ragged
+# last wave.
+@pytest.mark.parametrize("El,k,gate,G,TG,topn,renorm", [
+    (256, 8, "sigmoid", 1, 1, 2, True), (256, 8, "softmax", 1, 1, 2, False),
+    (256, 8, "sigmoid", 8, 3, 1, True), (512, 16, "softmax", 4, 2, 2, True),
+    (64, 6, "sigmoid", 16, 4, 2, True), (48, 5, "softmax", 3, 2, 2, True),
+    (16, 3, "sigmoid", 1, 1, 2, False), (160, 8, "sigmoid", 8, 4, 2, True),  # 160: falls back
+])
+def test_route_large_batches(El, k, gate, G, TG, topn, renorm):
+    rng = np.random.default_rng(El + k + G)
+    T = 2101
+    z = rng.standard_normal((T, El)).astype(np.float32)
+    check(T, k, El, z, gate=gate, n_groups=G, topk_groups=TG, group_topn=topn, renorm=renorm)
+    zt = (np.round(z * 2) / 2).astype(np.float32)     # exact ties
+    check(T, k, El, zt, gate=gate, n_groups=G, topk_groups=TG, group_topn=topn, renorm=renorm)
+
+
+def test_route_large_batch_bias_replicas_and_grid():
+    rng = np.random.default_rng(21)
+    El, E, T, k = 256, 288, 2500, 8
+    n = np.ones(El, np.int64)
+    n[rng.choice(El, 32, replace=False)] += 1
+    off = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    slots = rng.permutation(E).astype(np.int32)
+    z = rng.standard_normal((T, El)).astype(np.float32)
+    b = (-1.1 * np.log1p(rng.permutation(El))).astype(np.float32)
+    for nwg in (0, 1, 7, 300):
+        check(T, k, E, z, gate="sigmoid", n_groups=8, topk_groups=4, bias=b, rep_offsets=off,
+              rep_slots=slots, num_workgroups=nwg)
+
+
 def test_route_grid_size_invariance():
     w = make_workload("v3_skew", T=1000)
     x = w.extra
