@@ -131,7 +131,7 @@ KERNEL_KEYS = {
     "layout_count": r"::layout_count_kernel\(",
     "layout_scatter": r"::layout_scatter_kernel\(",
     "layout_small": r"::layout_small_kernel\(",
-    "route": r"::route_kernel<\d+>\(",
+    "route": r"::route(_rows)?_kernel<\d+>\(",
     "layout_dispatch_small": r"::layout_dispatch_small_kernel<(true|false)>\(",
     "combine_shared": r"::combine_kernel<true>\(",
     "combine_backward": r"::combine_backward_(wave|wg)_kernel\(",
