@@ -35,6 +35,30 @@ __device__ inline int32_t wave_sum(int32_t v) {
   return v;
 }
 
+// DPP controls (gfx9): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror,
+// row_mirror.  After these four steps of a commutative reduction every lane
+// of a 16-lane row holds the row's result.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ inline uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ inline uint32_t rdl(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+// Sum over the wave (32-bit, wrapping), uniform result: four DPP steps in
+// each row, then the four row sums.
+__device__ inline uint32_t wave_sum_u32(uint32_t v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  return (rdl(v, 0) + rdl(v, 16)) + (rdl(v, 32) + rdl(v, 48));
+}
+
 // OCP E4M3 ("fn") of a binary32 value, nearest-even, saturating at 448.
 // Normal results: round the binary32 significand to 3 bits on the bit
 // pattern and rebias the exponent (127 -> 7).  Below 2^-6 the E4M3 spacing is

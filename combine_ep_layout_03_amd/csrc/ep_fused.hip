@@ -9,15 +9,20 @@
 // routing handle while gating is unchanged).
 //
 // Design.  With T*k <= kFusedMaxPairs the whole index array is 8 KB or less,
-// so every single-wave workgroup reads all of it (L2-resident) and computes
-// the expert histogram and its exclusive scan in LDS itself: no workgroup
-// waits for another, and the layout costs no launch of its own.  A workgroup
-// then takes (token, segment) units like ep_dispatch; for its token's k pairs
-// it finds each pair's rank among the earlier pairs of the same expert by
-// counting matches in the register-held index array (a wave sum), which gives
-// exactly the stable slot of the two-pass layout.  Segment-0 units write their
-// token's slot_of / src_of entries; unit 0 writes the per-expert and per-rank
-// arrays and the error word.  The row payload is the same code as ep_dispatch.
+// so every single-wave workgroup reads all of it (coalesced, L2-resident) and
+// computes the expert histogram and its exclusive scan in LDS itself: no
+// workgroup waits for another, and the layout costs no launch of its own.  A
+// workgroup then takes (token, segment) units like ep_dispatch; for its
+// token's k pairs it finds each pair's rank among the earlier pairs of the
+// same expert by counting matches in the register-held index array -- eight
+// pairs at once, two counts per word, reduced by DPP row sums -- which gives
+// exactly the stable slot of the two-pass layout.  The unit's payload is
+// loaded first, so its latency overlaps the layout work.  Segment-0 units
+// write their token's slot_of / src_of entries; unit 0 writes the per-expert
+// and per-rank arrays and the error word.  The row payload is the same code
+// as ep_dispatch.  (Measured on MI355X at 128 tokens x 8: counting one pair
+// at a time, each a dependent load and a shuffle-based wave sum, took 5.8 of
+// this kernel's 11.8 us.)
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -29,6 +34,27 @@ using namespace dev;
 constexpr int kPL = kFusedMaxPairs / kWave;  // indices held per lane
 constexpr int kFp8SegBlocks = 8;             // as in ep_dispatch
 
+// One unit's slice of x: FP8 units take 16 channels per lane (two 16-byte
+// vectors), BF16 units one 16-byte chunk per lane (v1 unused).
+template <bool FP8>
+__device__ inline void load_payload(const uint16_t *__restrict__ x, int64_t t, int seg, int H,
+                                    int lane, u32x4 &v0, u32x4 &v1) {
+  v0 = u32x4{0u, 0u, 0u, 0u};
+  v1 = v0;
+  const uint16_t *xrow = x + t * H;
+  if (FP8) {
+    const int blk = seg * kFp8SegBlocks + lane / 8;
+    if (blk < H / 128) {
+      const int ch = blk * 128 + (lane % 8) * 16;
+      v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch));
+      v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch + 8));
+    }
+  } else {
+    const int c = seg * kWave + lane;
+    if (c < H / 8) v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow) + c);
+  }
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(kWave) void layout_dispatch_small_kernel(
     const int32_t *__restrict__ idx, const uint16_t *__restrict__ x, int32_t T, int32_t H,
@@ -37,25 +63,33 @@ __global__ __launch_bounds__(kWave) void layout_dispatch_small_kernel(
   const int lane = threadIdx.x;
   const int64_t P = (int64_t)T * k;
   const int32_t El = E / R;
+  const int nv = (int)((P + kWave - 1) / kWave);  // index registers in use
+  const int nb = H / 128, nch = H / 8;
+  const int nseg = FP8 ? (nb + kFp8SegBlocks - 1) / kFp8SegBlocks : (nch + kWave - 1) / kWave;
+  const int64_t units = (int64_t)T * nseg;
 
-  // every index, lane-contiguous: lane owns pairs [lane*kPL, lane*kPL + kPL)
+  // the first unit's payload, loaded now so that it overlaps the layout work
+  int64_t u = blockIdx.x;
+  u32x4 pv0, pv1;
+  if (u < units) load_payload<FP8>(x, u / nseg, (int)(u % nseg), H, lane, pv0, pv1);
+
+  // every index, coalesced: value i of this lane is pair i*64 + lane
   int32_t ev[kPL];
+  uint32_t bad = 0;
 #pragma unroll
   for (int i = 0; i < kPL; ++i) {
-    const int64_t p = (int64_t)lane * kPL + i;
-    ev[i] = (p < P) ? idx[p] : 0;
+    const int64_t p = (int64_t)i * kWave + lane;
+    ev[i] = (i < nv && p < P) ? idx[p] : 0;
+    if (i < nv && p < P && (uint32_t)ev[i] >= (uint32_t)E) ++bad;
   }
   for (int e = lane; e <= E; e += kWave) off[e] = 0;
   __syncthreads();
-  int32_t bad = 0;
 #pragma unroll
   for (int i = 0; i < kPL; ++i) {
-    if ((int64_t)lane * kPL + i < P) {
-      if ((uint32_t)ev[i] < (uint32_t)E) atomicAdd(&off[ev[i]], 1);
-      else ++bad;
-    }
+    const int64_t p = (int64_t)i * kWave + lane;
+    if (i < nv && p < P && (uint32_t)ev[i] < (uint32_t)E) atomicAdd(&off[ev[i]], 1);
   }
-  bad = wave_sum(bad);
+  bad = wave_sum_u32(bad);
   __syncthreads();
   {  // exclusive scan of off[0..E), off[E] = total
     const int per = (E + kWave - 1) / kWave;
@@ -90,27 +124,37 @@ __global__ __launch_bounds__(kWave) void layout_dispatch_small_kernel(
   }
   if (bad) return;  // uniform: nothing is dispatched for a bad index array
 
-  const int nb = H / 128, nch = H / 8;
-  const int nseg = FP8 ? (nb + kFp8SegBlocks - 1) / kFp8SegBlocks : (nch + kWave - 1) / kWave;
-  const int64_t units = (int64_t)T * nseg;
-  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+  for (; u < units; u += gridDim.x) {
     const int64_t t = u / nseg;
     const int seg = (int)(u % nseg);
-    // lane j < k: the slot of pair (t, j) = offset of its expert + number of
-    // earlier pairs with that expert (counted over every lane's indices)
-    int32_t my_slot = 0, my_e = 0;
-    for (int j = 0; j < k; ++j) {
-      const int64_t p = t * k + j;
-      const int32_t e = idx[p];  // uniform
-      int32_t c = 0;
+    if (u != (int64_t)blockIdx.x) load_payload<FP8>(x, t, seg, H, lane, pv0, pv1);
+    // lane j < k: the expert e of pair (t, j) and its slot = offset of e +
+    // the earlier pairs with e: those before the token's first pair t*k,
+    // counted for 8 of the token's experts at a time over every lane's
+    // indices (two counts per 32-bit word, each < P <= 2048, reduced by DPP
+    // row sums), plus the token's own earlier pairs with e
+    const int32_t tk = (int32_t)(t * k);
+    const int32_t my_e = (lane < k) ? idx[tk + lane] : 0;
+    int32_t my_slot = 0;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      int32_t ej[8];
 #pragma unroll
-      for (int i = 0; i < kPL; ++i) c += ((int64_t)lane * kPL + i < p && ev[i] == e) ? 1 : 0;
-      c = wave_sum(c);
-      if (lane == j) {
-        my_slot = off[e] + c;
-        my_e = e;
+      for (int jj = 0; jj < 8; ++jj) ej[jj] = (j0 + jj < k) ? (int32_t)rdl((uint32_t)my_e, j0 + jj) : -1;
+      uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < kPL; ++i) {
+        if (i < nv && i * kWave + lane < tk) {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) c[jj / 2] += (ev[i] == ej[jj]) ? (1u << (16 * (jj & 1))) : 0u;
+        }
       }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) c[q] = wave_sum_u32(c[q]);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if (lane == j0 + jj) my_slot = off[ej[jj]] + (int32_t)((c[jj / 2] >> (16 * (jj & 1))) & 0xFFFFu);
     }
+    for (int j = 0; j < k; ++j) my_slot += (j < lane && (int32_t)rdl((uint32_t)my_e, j) == my_e) ? 1 : 0;
     uint64_t dst = 0, sdst = 0;
     if (lane < k) {
       const int32_t r = my_e / El;
@@ -130,14 +174,8 @@ __global__ __launch_bounds__(kWave) void layout_dispatch_small_kernel(
       const int blk = seg * kFp8SegBlocks + lane / 8;
       const bool valid = blk < nb;
       const int ch = blk * 128 + (lane % 8) * 16;
-      const uint16_t *xrow = x + t * H;
-      u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-      if (valid) {
-        v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch));
-        v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch + 8));
-      }
       float s;
-      const u32x4 q = quant_block16(v0, v1, s);
+      const u32x4 q = quant_block16(pv0, pv1, s);
       for (int j = 0; j < k; ++j) {
         uint8_t *d = reinterpret_cast<uint8_t *>(readlane64(dst, j));
         float *sd = reinterpret_cast<float *>(readlane64(sdst, j));
@@ -149,11 +187,9 @@ __global__ __launch_bounds__(kWave) void layout_dispatch_small_kernel(
     } else {
       const int c = seg * kWave + lane;
       const bool ok = c < nch;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + t * H) + c);
       for (int j = 0; j < k; ++j) {
         u32x4 *d = reinterpret_cast<u32x4 *>(readlane64(dst, j));
-        if (ok) __builtin_nontemporal_store(v, d + c);
+        if (ok) __builtin_nontemporal_store(pv0, d + c);
       }
     }
   }

@@ -37,22 +37,8 @@ namespace {
 
 using namespace dev;
 
-// DPP controls (gfx9): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror,
-// row_mirror.  After these four steps every lane of a 16-lane row holds the
-// row's reduction.
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-
-template <int CTRL>
-__device__ inline uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
-}
-
 __device__ inline uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 __device__ inline uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
-
-__device__ inline uint32_t rdl(uint32_t v, int lane) {
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
-}
 
 // Maximum over the wave (unsigned), uniform result.
 __device__ inline uint32_t wave_max_u32(uint32_t v) {

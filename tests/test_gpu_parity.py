@@ -397,7 +397,8 @@ def test_layout_dispatch_matches_oracle(name, T):
 
 
 @pytest.mark.parametrize("case", [("E2048", 100, 8, 2048, 64, True), ("k32", 64, 32, 64, 8, False),
-                                  ("one_expert", 256, 8, 16, 4, True), ("R1", 300, 2, 8, 1, False)],
+                                  ("one_expert", 256, 8, 16, 4, True), ("R1", 300, 2, 8, 1, False),
+                                  ("k12_repeats", 150, 12, 24, 4, True)],
                          ids=lambda c: c[0])
 def test_layout_dispatch_edge_cases(case):
     name, T, k, E, R, fp8 = case
