@@ -151,3 +151,31 @@ def test_backward_rejects_half_given_grad_w():
     with pytest.raises(ep.EpError) as ei:
         ep.ep_combine_backward(run.cfg, run.h, run.idx, g, run.wts, rows, rows, None, run.cap)
     assert ei.value.status == ep.EP_ERR_INVALID_ARG
+
+
+def test_entry_points_write_nothing_after_a_bad_index():
+    """An index outside [0,E) sets EP_DEVERR_INDEX in the handle; the shared-
+    expert combine, the combine backward and the SiLU re-quantization read the
+    error word first and leave every output byte untouched."""
+    from test_gpu_parity import custom
+    T, H, k, E, R, I = 64, 256, 4, 16, 4, 256
+    idx = np.random.default_rng(3).integers(0, E, (T, k))
+    idx[17, 1] = E + 5
+    w = custom("bad", T, H, k, E, R, False, idx)
+    run = GpuRun(w).layout()
+    assert int(run.handle_np()["error_flag"][0]) & ep.EP_DEVERR_INDEX
+    say("entry points after a bad index")
+    rnd = lambda *shape: to_dev(bf16_from_f32(np.ones(shape, np.float32)))
+    ys = [rnd(run.cap, H) for _ in range(R)]
+    out = torch.full((T, H), 0x5A5A, dtype=torch.int16, device="cuda")
+    ep.ep_combine_shared(run.cfg, run.h, run.idx, ys, run.wts, rnd(T, H), out, run.cap)
+    grows = [torch.full((run.cap, H), 0x5A5A, dtype=torch.int16, device="cuda") for _ in range(R)]
+    gw = torch.full((T, k), 7.0, dtype=torch.float32, device="cuda")
+    ep.ep_combine_backward(run.cfg, run.h, run.idx, rnd(T, H), run.wts, ys, grows, gw, run.cap)
+    q = [torch.full((run.cap, I), POISON, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    s = [torch.full((run.cap, I // 128), 7.0, dtype=torch.float32, device="cuda") for _ in range(R)]
+    ep.ep_silu_mul_quant(run.cfg, run.h, I, [rnd(run.cap, 2 * I) for _ in range(R)], q, s, run.cap)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0x5A5A)
+    assert all(torch.all(g == 0x5A5A) for g in grows) and torch.all(gw == 7.0)
+    assert all(torch.all(t == POISON) for t in q) and all(torch.all(t == 7.0) for t in s)
