@@ -24,6 +24,7 @@ struct ScalePtrs {
 // Layout plan: the P = T*k pairs are cut into C chunks of S pairs; one
 // wavefront owns one chunk in both layout kernels.
 struct LayoutPlan {
+  bool tiny;   // one single-wave workgroup per 64 pairs (P <= kFusedMaxPairs)
   bool small;  // single-workgroup path
   int64_t P;
   int32_t S;  // pairs per chunk (multiple of 64)

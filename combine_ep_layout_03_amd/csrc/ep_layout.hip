@@ -19,9 +19,10 @@
 //              popcount(match & lanes-below), and the group's highest lane
 //              advances the expert's running base in LDS.  This reproduces
 //              "slot = offset[e] + #earlier pairs of e" exactly.
-// Small problems (P <= kSmallMaxPairs, E <= kSmallMaxExperts, e.g. decode
-// batches) run all three phases in ONE launch of one 16-wave workgroup (its
-// waves are the chunks).  Larger ones use two launches: a count kernel writes
+// Decode-sized problems (P <= kFusedMaxPairs) run in ONE launch of one
+// single-wave workgroup per 64 pairs, each counting every pair itself.  Small
+// problems (P <= kSmallMaxPairs, E <= kSmallMaxExperts) run all three phases
+// in ONE launch of one 16-wave workgroup (its waves are the chunks).  Larger ones use two launches: a count kernel writes
 // a [C/4][E+1][4] table of chunk histograms (a workgroup's 4 chunks are one
 // 16-byte group per expert; entry E counts bad indices) to the workspace,
 // and a scatter kernel in which every workgroup reads the whole table --
@@ -39,6 +40,15 @@ namespace ep {
 LayoutPlan plan_layout(int64_t P, int E) {
   LayoutPlan p{};
   p.P = P;
+  if (P <= kFusedMaxPairs) {
+    // single launch: one single-wave workgroup per 64 pairs
+    p.tiny = true;
+    p.S = kWave;
+    p.C = (int32_t)((P + kWave - 1) / kWave);
+    p.workgroups = p.C;
+    p.workspace_bytes = 256;  // unused; a minimal buffer keeps the contract uniform
+    return p;
+  }
   if (P <= kSmallMaxPairs && E <= kSmallMaxExperts) {
     // single launch: G workgroups of kSmallWaves waves, ~4096 pairs each
     int64_t G = (P + 4095) / 4096;
@@ -266,6 +276,97 @@ __device__ void wave_walk(const int32_t *__restrict__ idx, int64_t p0, int64_t p
   }
 }
 
+// Single-launch layout for P <= kFusedMaxPairs (decode batches): workgroup g
+// (one wave) owns pairs [64g, 64g + 64).  Every workgroup holds all P indices
+// in registers (coalesced loads, at most kTinyPL per lane) and counts in LDS
+// the expert totals and the pairs before its own 64, scans the totals, and
+// ranks its own pairs with the ballot match; no workgroup waits for another.
+// (The one-workgroup small path took 8 us at 1024 pairs, a chain of
+// barriers and per-wave prefix loops.)
+constexpr int kTinyPL = (int)(kFusedMaxPairs / kWave);
+
+__global__ __launch_bounds__(kWave) void layout_tiny_kernel(const int32_t *__restrict__ idx,
+                                                            int64_t P, int32_t E, int32_t R,
+                                                            ep_layout_t h) {
+  extern __shared__ int32_t lds[];
+  int32_t *tot = lds;          // [E+1] totals, then exclusive offsets
+  int32_t *pre = lds + E + 1;  // [E]   pairs of e before this workgroup's 64
+  const int lane = threadIdx.x;
+  const int nv = (int)((P + kWave - 1) / kWave);
+  const int64_t p = (int64_t)blockIdx.x * kWave + lane;  // this lane's own pair
+  const bool own = p < P;
+  const int32_t pe = own ? idx[p] : 0;
+  int32_t ev[kTinyPL];
+  uint32_t bad = 0;
+#pragma unroll
+  for (int i = 0; i < kTinyPL; ++i) {
+    const int64_t q = (int64_t)i * kWave + lane;
+    ev[i] = (i < nv && q < P) ? idx[q] : 0;
+    if (i < nv && q < P && (uint32_t)ev[i] >= (uint32_t)E) ++bad;
+  }
+  for (int e = lane; e < 2 * E + 1; e += kWave) lds[e] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kTinyPL; ++i) {
+    const int64_t q = (int64_t)i * kWave + lane;
+    if (i < nv && q < P && (uint32_t)ev[i] < (uint32_t)E) {
+      atomicAdd(&tot[ev[i]], 1);
+      if (i < (int)blockIdx.x) atomicAdd(&pre[ev[i]], 1);  // pair q = 64i + lane precedes 64g
+    }
+  }
+  bad = dev::wave_sum_u32(bad);
+  __syncthreads();
+  {  // exclusive scan of tot[0..E), tot[E] = total
+    const int per = (E + kWave - 1) / kWave;
+    const int b = (lane * per < E) ? lane * per : E;
+    const int end = (b + per < E) ? b + per : E;
+    int32_t s = 0;
+    for (int i = b; i < end; ++i) s += tot[i];
+    const int32_t incl = wave_inclusive_scan(s, lane);
+    int32_t run = incl - s;
+    for (int i = b; i < end; ++i) {
+      const int32_t v = tot[i];
+      tot[i] = run;
+      run += v;
+    }
+    if (lane == kWave - 1) tot[E] = incl;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    const int32_t El = E / R;
+    for (int e = lane; e < E; e += kWave) {
+      h.expert_counts[e] = tot[e + 1] - tot[e];
+      h.expert_offsets[e] = tot[e];
+    }
+    for (int r = lane; r < R; r += kWave) {
+      h.rank_offsets[r] = tot[r * El];
+      h.rank_counts[r] = tot[(r + 1) * El] - tot[r * El];
+    }
+    if (lane == 0) {
+      h.expert_offsets[E] = tot[E];
+      h.rank_offsets[R] = tot[E];
+      h.error_flag[0] = bad ? (int32_t)EP_DEVERR_INDEX : 0;
+    }
+  }
+  if (bad) return;  // uniform: the handle's slots are unspecified on error
+  // lanes whose expert matches this lane's in every bit: m &= (bit ? B : ~B)
+  const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
+  uint64_t m = __ballot(own);
+  for (int b = 0; b < nbits; ++b) {
+    const uint32_t bit = ((uint32_t)pe >> b) & 1u;
+    const uint64_t bb = __ballot(bit != 0u);
+    const uint32_t flip = bit - 1u;
+    m &= bb ^ (((uint64_t)flip << 32) | flip);
+  }
+  if (own) {
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    const int32_t slot = tot[pe] + pre[pe] + __popcll(m & below);
+    h.slot_of[p] = slot;
+    if ((uint64_t)(uint32_t)slot < (uint64_t)P) h.src_of[slot] = (int32_t)p;
+    else atomicOr(h.error_flag, (int32_t)EP_DEVERR_INTERNAL);  // cannot happen; never write out of range
+  }
+}
+
 constexpr int kSmallThreads = kSmallWaves * kWave;
 constexpr int kSmallRounds = 2;  // int4 loads per thread per batch (2 x 4096 pairs: P <= 8192 is one batch)
 
@@ -434,6 +535,12 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
 hipError_t launch_layout(const ep_config &c, const LayoutPlan &plan, const int32_t *topk_idx,
                          const ep_layout_t &h, void *workspace, hipStream_t s) {
   const int E = c.num_experts;
+  if (plan.tiny) {
+    hipLaunchKernelGGL(layout_tiny_kernel, dim3(plan.workgroups), dim3(kWave),
+                       (size_t)(2 * E + 1) * sizeof(int32_t), s, topk_idx, plan.P, E, c.num_ranks,
+                       h);
+    return hipGetLastError();
+  }
   if (plan.small) {
     const size_t lds = (((size_t)(kSmallWaves + 2) * E + 1 + 2 * kSmallWaves + 3) / 4 * 4 +
                         (size_t)kSmallWaves * kSmallStage) * sizeof(int32_t);

@@ -84,6 +84,11 @@ def layout_edge_cases():
     cases.append(("max_topk", 97, 32, 64, 8, rng.integers(0, 64, (97, 32))))
     cases.append(("max_experts", 2000, 8, 2048, 64, rng.integers(0, 2048, (2000, 8))))
     cases.append(("many_chunks_capped", 40000, 8, 2048, 8, rng.integers(0, 2048, (40000, 8))))
+    # the one-wave-per-64-pairs path (P <= 2048) at its limits, and the next path just past them
+    cases.append(("tiny_path_max", 256, 8, 288, 36, rng.integers(0, 288, (256, 8))))
+    cases.append(("tiny_ragged_E2048", 199, 8, 2048, 64, rng.integers(0, 2048, (199, 8))))
+    cases.append(("tiny_one_expert", 100, 8, 16, 4, np.full((100, 8), 5)))
+    cases.append(("small_path_min", 683, 3, 64, 8, rng.integers(0, 64, (683, 3))))
     # the single-workgroup path at its limits, and the two-launch path just past them
     cases.append(("small_path_max", 1024, 8, 384, 8, rng.integers(0, 384, (1024, 8))))
     cases.append(("small_path_ragged", 1021, 8, 384, 16, rng.integers(0, 384, (1021, 8))))
