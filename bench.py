@@ -131,6 +131,7 @@ KERNEL_KEYS = {
     "layout_count": r"::layout_count_kernel\(",
     "layout_scatter": r"::layout_scatter_kernel\(",
     "layout_small": r"::layout_small_kernel\(",
+    "layout_tiny": r"::layout_tiny_kernel\(",
     "route": r"::route(_rows)?_kernel<\d+>\(",
     "layout_dispatch_small": r"::layout_dispatch_small_kernel<(true|false)>\(",
     "combine_shared": r"::combine_kernel<true>\(",
