@@ -13,6 +13,10 @@ Prints ONE JSON line (rank 0, N=1):
   roofline     = the dominant kernel (combine): algorithmic bytes per launch /
                  its mean HIP-event duration, against 8 TB/s HBM peak
   cpu_baseline = the CPU oracle (single thread) on a bounded sample
+  extras       = the other entry points timed in the same run (router, decode-
+                 style steps, shared-expert combine, combine backward, SiLU
+                 re-quantization); --no-extras skips them
+--summarize writes the profiles/ summaries from rocprofv3 CSV output.
 """
 from __future__ import annotations
 

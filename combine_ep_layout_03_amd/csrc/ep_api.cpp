@@ -3,6 +3,7 @@
 // enqueues nothing when it fails; the kernels are in the .hip files beside it
 // (layout, dispatch, combine, the fused decode path, the expert activation and
 // the router).
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 

@@ -29,12 +29,6 @@ __device__ inline int32_t wave_inclusive_scan(int32_t v, int lane) {
   return v;
 }
 
-__device__ inline int32_t wave_sum(int32_t v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
 // DPP controls (gfx9): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror,
 // row_mirror.  After these four steps of a commutative reduction every lane
 // of a 16-lane row holds the row's result.
@@ -59,27 +53,6 @@ __device__ inline uint32_t wave_sum_u32(uint32_t v) {
   return (rdl(v, 0) + rdl(v, 16)) + (rdl(v, 32) + rdl(v, 48));
 }
 
-// OCP E4M3 ("fn") of a binary32 value, nearest-even, saturating at 448.
-// Normal results: round the binary32 significand to 3 bits on the bit
-// pattern and rebias the exponent (127 -> 7).  Below 2^-6 the E4M3 spacing is
-// 2^-9, so the code is rint(|v| * 2^9) (the scaling is exact).  This is the
-// software statement of the conversion; the quantizers below use gfx950's
-// v_cvt_pk_fp8_f32, which gives the same byte for every binary32 value with
-// |v| <= 450 (all 2^31 + signs checked on MI355X); quotients x/s never leave
-// that range (|x/s| <= 448 * (1 + 2^-23)).
-__device__ inline uint32_t e4m3_code(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a >= 0x43E00000u)  // |v| >= 448 (NaN is never produced here)
-    return sign | (a > 0x7F800000u ? 0x7Fu : 0x7Eu);
-  if (a < 0x3C800000u)   // |v| < 2^-6
-    return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;  // exp8 | mant3, rounded
-  const uint32_t code = r - (120u << 3);
-  return sign | (code < 0x7Eu ? code : 0x7Eu);
-}
-
 // max over the low 15 bits (|x| of bf16, monotone for non-NaN) of 8 bf16.
 __device__ inline uint32_t bf16_absbits_max(u32x4 v, uint32_t m) {
 #pragma unroll
@@ -91,8 +64,13 @@ __device__ inline uint32_t bf16_absbits_max(u32x4 v, uint32_t m) {
   return m;
 }
 
-// Four binary32 values (each |v| <= 448 * (1 + 2^-23)) -> four E4M3 codes in
-// one dword, byte i = code of a_i (the hardware conversion, nearest-even).
+// Four binary32 values (each |v| <= 448 * (1 + 2^-23)) -> four OCP E4M3
+// ("fn": bias 7, max 448, no infinity) codes in one dword, byte i = code of
+// a_i, by gfx950's v_cvt_pk_fp8_f32: nearest with ties to even, saturating at
+// 448, signed zeros kept.  On MI355X it was compared, over every binary32
+// pattern with |v| <= 450 (both signs), with an encoder that rounds the
+// binary32 significand to 3 bits on the bit pattern (rint(|v| * 2^9) below
+// 2^-6): no mismatch.  A block quotient x/s never exceeds 448 * (1 + 2^-23).
 __device__ inline uint32_t e4m3_pack4(float a0, float a1, float a2, float a3) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, w, true);

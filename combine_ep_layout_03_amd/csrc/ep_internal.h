@@ -29,8 +29,9 @@ struct LayoutPlan {
   int64_t P;
   int32_t S;  // pairs per chunk (multiple of 64)
   int32_t C;  // chunks
-  int32_t workgroups;  // ceil(C / kLayoutWaves)
-  size_t workspace_bytes;  // ceil(C/4)*4 * (E + 1) * 4: chunk histograms [C/4][E+1][4]
+  int32_t workgroups;  // launch grid: C (tiny, small) or ceil(C / kLayoutWaves) (two-launch)
+  size_t workspace_bytes;  // two-launch: ceil(C/4)*4 * (E + 1) * 4, chunk histograms
+                           // [C/4][E+1][4]; one-launch paths: 256 (unused)
 };
 
 constexpr int kWave = 64;
@@ -41,7 +42,8 @@ constexpr int kRowWaves = 1;     // wavefronts per dispatch / combine workgroup
 constexpr int kSmallWaves = 16;  // wavefronts of the single-workgroup layout
 constexpr int64_t kSmallMaxPairs = 8192;    // T*k limit of the single-launch layout
 constexpr int kSmallMaxExperts = 384;       // E limit of the single-launch layout (LDS <= 64 KB)
-constexpr int64_t kFusedMaxPairs = 2048;    // T*k limit of the one-launch layout + dispatch
+constexpr int64_t kFusedMaxPairs = 2048;    // T*k limit of the one-launch layout + dispatch and
+                                            // of the one-wave-per-64-pairs layout
 
 LayoutPlan plan_layout(int64_t P, int E);
 
