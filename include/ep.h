@@ -161,8 +161,8 @@ size_t ep_layout_workspace_bytes(const ep_config *cfg /*(host)*/);
  * other handle arrays are then unspecified).  `workspace` must hold
  * ep_layout_workspace_bytes(cfg) bytes and be 16-byte aligned (any device
  * allocation is; otherwise EP_ERR_INVALID_ARG); its contents on entry do not
- * matter and are clobbered.  Launches one kernel for T*k <= 8192 with
- * E <= 384, else two, on `stream`. */
+ * matter and are clobbered.  Launches one kernel for T*k <= 2048, or for
+ * T*k <= 8192 with E <= 384, else two, on `stream`. */
 ep_status ep_layout(const ep_config *cfg /*(host)*/, const int32_t *topk_idx,
                     const ep_layout_t *h /*(host struct of device pointers)*/,
                     void *workspace, hipStream_t stream);
