@@ -155,6 +155,24 @@ def test_route_large_batch_bias_replicas_and_grid():
               rep_slots=slots, num_workgroups=nwg)
 
 
+@pytest.mark.parametrize("T,El,k,G,TG", [(300, 256, 8, 1, 1), (2200, 256, 8, 8, 4), (70, 64, 6, 4, 2)])
+@pytest.mark.parametrize("gate", ["softmax", "sigmoid"])
+def test_route_non_finite_logits_give_valid_picks(T, El, k, G, TG, gate):
+    """NaN / +-inf logits leave the choice unspecified, but every token still
+    gets k distinct experts inside its kept groups, on both router kernels."""
+    rng = np.random.default_rng(T + El)
+    z = rng.standard_normal((T, El)).astype(np.float32)
+    z[rng.random(z.shape) < 0.2] = np.nan
+    z[rng.random(z.shape) < 0.1] = np.inf
+    z[rng.random(z.shape) < 0.1] = -np.inf
+    say(f"route non-finite T={T} El={El} G={G} {gate}")
+    gi, _ = run_route(T, k, El, z, gate=gate, n_groups=G, topk_groups=TG)
+    gs = El // G
+    assert np.all((gi >= 0) & (gi < El))
+    assert all(len(set(r)) == k for r in gi)
+    assert all(len(set(r // gs)) <= TG for r in gi)
+
+
 def test_route_grid_size_invariance():
     w = make_workload("v3_skew", T=1000)
     x = w.extra

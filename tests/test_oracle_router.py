@@ -184,3 +184,32 @@ def test_router_rejects_bad_parameters(kw):
     args.update(kw)
     with pytest.raises(oracle.OracleError):
         oracle.route(np.zeros((2, 16), np.float32), **args)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_router_properties_on_random_shapes(seed):
+    """Invariants on random shapes, including non-finite logits (for which the
+    choice is unspecified): k distinct ids in [0, El) per token, all inside
+    the TG kept groups; finite logits with renormalization give weights that
+    sum to 1."""
+    rng = np.random.default_rng(100 + seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    gs = int(rng.integers(1, 9))
+    El = G * gs
+    TG = int(rng.integers(1, G + 1))
+    k = int(rng.integers(1, min(TG * gs, 16) + 1))
+    T = int(rng.integers(1, 200))
+    gate = ["softmax", "sigmoid"][seed % 2]
+    z = (rng.standard_normal((T, El)) * 4).astype(np.float32)
+    idx, w = oracle.route(z, k, gate=gate, n_groups=G, topk_groups=TG, renorm=True)
+    assert np.all((idx >= 0) & (idx < El))
+    assert all(len(set(r)) == k for r in idx)
+    assert all(len(set(r // gs)) <= TG for r in idx)
+    assert np.allclose(w.sum(axis=1, dtype=np.float64), 1.0, atol=1e-5)
+    zb = z.copy()
+    zb[rng.random(z.shape) < 0.2] = np.nan
+    zb[rng.random(z.shape) < 0.1] = np.inf
+    zb[rng.random(z.shape) < 0.1] = -np.inf
+    idx, _ = oracle.route(zb, k, gate=gate, n_groups=G, topk_groups=TG, renorm=True)
+    assert np.all((idx >= 0) & (idx < El))
+    assert all(len(set(r)) == k for r in idx)
