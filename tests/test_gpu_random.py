@@ -8,6 +8,11 @@ with E <= 384, two launches) and ragged tails in combinations the hand-picked
 cases do not.  Sizes stay small enough for the oracle to finish in a second.
 The bar is the usual one: layout and dispatch bytes exact, combine within
 1e-2 relative (bit mismatches reported).
+
+Two more sweeps draw random router configurations (gate, groups, kept
+groups, group score form, bias, replicas; both router kernels by batch size)
+checked bit for bit, and random shapes through the shared-expert combine,
+both combine-backward paths and the SiLU re-quantization.
 """
 import numpy as np
 import pytest
@@ -94,3 +99,83 @@ def test_random_shapes(seed):
     ep.ep_layout_dispatch(run2.cfg, run2.idx, run2.h, run2.ws, run2.x, run2.recv.x, run2.recv.scales,
                           run2.cap)
     check_path(w, run2, "layout_dispatch")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_router(seed):
+    """Random router configurations (both kernels, every group form, bias,
+    replicas) bit for bit against the oracle."""
+    from test_gpu_router import check
+    rng = np.random.default_rng(2000 + seed)
+    G = int(rng.choice([1, 1, 2, 4, 8, 16]))
+    gs = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    El = min(G * gs, 512)
+    gs = El // G
+    TG = int(rng.integers(1, G + 1))
+    k = int(rng.integers(1, min(TG * gs, 16) + 1))
+    T = int(rng.choice([1, 37, 300, 2048, 2300]))
+    gate = ["softmax", "sigmoid"][int(rng.integers(0, 2))]
+    z = (rng.standard_normal((T, El)) * float(rng.choice([0.5, 2, 8]))).astype(np.float32)
+    kw = dict(gate=gate, n_groups=G, topk_groups=TG, group_topn=int(rng.integers(1, 3)),
+              renorm=bool(rng.integers(0, 2)))
+    E = El
+    if rng.integers(0, 2):
+        kw["bias"] = (rng.standard_normal(El) * 0.5).astype(np.float32)
+    if rng.integers(0, 2):
+        n = 1 + rng.integers(0, 3, El)
+        kw["rep_offsets"] = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        E = int(kw["rep_offsets"][-1])
+        kw["rep_slots"] = rng.permutation(E).astype(np.int32)
+    check(T, k, E, z, **kw)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shared_backward_and_silu(seed):
+    """Random shapes through the shared-expert combine, the combine backward
+    (both paths) and the SiLU re-quantization against the oracle."""
+    from test_gpu_parity import custom
+    from test_gpu_backward import check_backward
+    from gpu_util import rows_to_dev, to_dev
+    from workloads import bf16_from_f32
+    rng = np.random.default_rng(3000 + seed)
+    R = int(rng.choice([1, 2, 8, 36]))
+    E = R * int(rng.choice([1, 4, 8]))
+    k = int(rng.integers(1, min(16, 2 * E) + 1))
+    T = int(rng.choice([5, 130, 1500, 2500])) + int(rng.integers(0, 3))
+    H = 8 * int(rng.integers(1, 200))
+    w = custom(f"rsb{seed}", T, H, k, E, R, False, rng.integers(0, E, (T, k)), seed=seed)
+    say(f"random shared/backward {seed}: T={T} H={H} k={k} E={E} R={R}")
+    run = GpuRun(w).layout()
+    L = oracle.layout(w.topk_idx, w.E, w.R)
+    y = make_expert_rows(w.P, w.H, seed=seed + 9)
+    ys = [y[L.rank_offsets[r]:L.rank_offsets[r + 1]] for r in range(w.R)]
+    shared = bf16_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ep.ep_combine_shared(run.cfg, run.h, run.idx, rows_to_dev(run.cap, H, ys), run.wts, to_dev(shared),
+                         out, run.cap)
+    torch.cuda.synchronize()
+    ref = oracle.combine_shared(ys, w.topk_idx, L, w.topk_w, shared)
+    assert rel_err(u16(out), ref) <= 1e-2
+    check_backward(w, run, L, ys)
+    # SiLU re-quantization on the same layout: I a multiple of 128
+    I = 128 * int(rng.integers(1, 5))
+    act = bf16_from_f32((rng.standard_normal((w.P, 2 * I)) * 2).astype(np.float32))
+    act_r = [act[L.rank_offsets[r]:L.rank_offsets[r + 1]] for r in range(w.R)]
+    qs = [torch.full((run.cap, I), POISON, dtype=torch.uint8, device="cuda") for _ in range(w.R)]
+    ss = [torch.full((run.cap, I // 128), float("nan"), dtype=torch.float32, device="cuda")
+          for _ in range(w.R)]
+    ep.ep_silu_mul_quant(run.cfg, run.h, I, rows_to_dev(run.cap, 2 * I, act_r), qs, ss, run.cap)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.silu_mul_quant(act)
+    a_ref = oracle.silu_mul(act).astype(np.float64)
+    for r in range(w.R):
+        n, lo = int(L.rank_counts[r]), int(L.rank_offsets[r])
+        q, s = qs[r].cpu().numpy(), ss[r].cpu().numpy()
+        assert np.all(q[n:] == POISON) and np.all(np.isnan(s[n:]))
+        q, s = q[:n], s[:n].astype(np.float64)
+        sr, ar = s_ref[lo:lo + n].astype(np.float64), a_ref[lo:lo + n]
+        assert np.all(np.abs(s - sr) <= 1e-6 * np.abs(sr))
+        sg = np.repeat(s, 128, axis=1)
+        dec = oracle.e4m3_decode(q).astype(np.float64) * sg
+        bound = np.maximum(2.0 ** -4 * np.abs(ar), 2.0 ** -10 * sg) * (1 + 1e-5) + 1e-6 * (np.abs(ar) + sg)
+        assert np.all(np.abs(dec - ar) <= bound), r
