@@ -126,8 +126,12 @@ int64_t ep_recv_capacity_rows(const ep_config *cfg) {
 
 size_t ep_layout_workspace_bytes(const ep_config *cfg) {
   if (!config_ok(cfg)) return 0;
-  return ep::plan_layout((int64_t)cfg->num_tokens * cfg->num_topk, cfg->num_experts)
-      .workspace_bytes;
+  // the larger of ep_layout's chunk table and ep_route_layout's router-counted one
+  const size_t a =
+      ep::plan_layout((int64_t)cfg->num_tokens * cfg->num_topk, cfg->num_experts).workspace_bytes;
+  const size_t b =
+      ep::plan_route_count(cfg->num_tokens, cfg->num_topk, cfg->num_experts).workspace_bytes;
+  return a > b ? a : b;
 }
 
 ep_status ep_layout(const ep_config *cfg, const int32_t *topk_idx, const ep_layout_t *h,
@@ -276,10 +280,10 @@ ep_status ep_route_layout(const ep_config *cfg, const ep_router_t *router, const
                                topk_weights);
   if (st != EP_OK) return st;
   if (!handle_ok(h) || !workspace_ok(workspace)) return EP_ERR_INVALID_ARG;
-  st = ep_route(cfg, router, logits, bias, replica_offsets, replica_slots, topk_idx, topk_weights,
-                stream);
-  if (st != EP_OK) return st;
-  return ep_layout(cfg, topk_idx, h, workspace, stream);
+  trace("route_layout", cfg);
+  return from_hip(ep::launch_route_layout(*cfg, *router, logits, bias, replica_offsets,
+                                          replica_slots, topk_idx, topk_weights, *h, workspace,
+                                          stream));
 }
 
 }  // extern "C"

@@ -27,8 +27,9 @@ struct LayoutPlan {
   bool tiny;   // one single-wave workgroup per 64 pairs (P <= kFusedMaxPairs)
   bool small;  // single-workgroup path
   int64_t P;
-  int32_t S;  // pairs per chunk (multiple of 64)
-  int32_t C;  // chunks
+  int32_t S;  // pairs per chunk (multiple of 64; k * tpc for the router-counted table)
+  int32_t C;  // chunks (0: no such plan)
+  int32_t tpc;  // router-counted table only: tokens per chunk (one router workgroup each)
   int32_t workgroups;  // launch grid: C (tiny, small) or ceil(C / kLayoutWaves) (two-launch)
   size_t workspace_bytes;  // two-launch: ceil(C/4)*4 * (E + 1) * 4, chunk histograms
                            // [C/4][E+1][4]; one-launch paths: 256 (unused)
@@ -47,10 +48,25 @@ constexpr int64_t kFusedMaxPairs = 2048;    // T*k limit of the one-launch layou
 
 LayoutPlan plan_layout(int64_t P, int E);
 
+// The router can count the layout's chunk table itself when one router
+// workgroup (kRouteCountWaves waves, four tokens each per step) routes exactly
+// one chunk of tpc tokens; then only the scatter kernel follows.  The plan has
+// C = 0 where the two-launch layout does not apply (decode and small sizes)
+// or E > kRouteCountMaxExperts.  C <= kLayoutMaxChunks.
+constexpr int kRouteCountWaves = 8;
+constexpr int kRouteCountStep = kRouteCountWaves * 4;  // tokens a router workgroup routes per step
+constexpr int kRouteCountMaxExperts = 512;
+LayoutPlan plan_route_count(int64_t T, int k, int E);
+
 // Launchers (no validation; the C ABI validates first).  Return hipError_t of
 // the launch.
 hipError_t launch_layout(const ep_config &c, const LayoutPlan &plan, const int32_t *topk_idx,
                          const ep_layout_t &h, void *workspace, hipStream_t s);
+
+// The scatter kernel alone, for a table the router counted (plan_route_count).
+hipError_t launch_layout_scatter(const ep_config &c, const LayoutPlan &plan,
+                                 const int32_t *topk_idx, const ep_layout_t &h, void *workspace,
+                                 hipStream_t s);
 
 hipError_t launch_dispatch(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
                            const void *x, const RankPtrs &rx, const ScalePtrs &rs,
@@ -77,6 +93,14 @@ hipError_t launch_layout_dispatch_small(const ep_config &c, const int32_t *topk_
 hipError_t launch_route(const ep_config &c, const ep_router_t &rt, const float *logits,
                         const float *bias, const int32_t *rep_off, const int32_t *rep_slots,
                         int32_t *topk_idx, float *topk_w, hipStream_t s);
+
+// ep_route_layout: the counting router + scatter where plan_route_count and
+// the four-tokens-per-wave router apply (and num_workgroups is 0), else
+// launch_route then launch_layout.
+hipError_t launch_route_layout(const ep_config &c, const ep_router_t &rt, const float *logits,
+                               const float *bias, const int32_t *rep_off,
+                               const int32_t *rep_slots, int32_t *topk_idx, float *topk_w,
+                               const ep_layout_t &h, void *workspace, hipStream_t s);
 
 hipError_t launch_unpermute(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
                             const RankCPtrs &ry, void *out, int64_t capacity_rows, hipStream_t s);

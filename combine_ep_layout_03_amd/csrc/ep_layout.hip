@@ -82,6 +82,23 @@ LayoutPlan plan_layout(int64_t P, int E) {
   return p;
 }
 
+LayoutPlan plan_route_count(int64_t T, int k, int E) {
+  const LayoutPlan lp = plan_layout(T * k, E);
+  LayoutPlan p{};
+  if (lp.tiny || lp.small || E > kRouteCountMaxExperts) return p;
+  // the fewest steps per workgroup that keep C <= kLayoutMaxChunks
+  const int64_t per = (T + kRouteCountStep - 1) / kRouteCountStep;
+  const int64_t steps = (per + kLayoutMaxChunks - 1) / kLayoutMaxChunks;
+  const int64_t tpc = steps * kRouteCountStep;
+  p.P = T * k;
+  p.tpc = (int32_t)tpc;
+  p.S = (int32_t)(tpc * k);
+  p.C = (int32_t)((T + tpc - 1) / tpc);
+  p.workgroups = (p.C + kLayoutWaves - 1) / kLayoutWaves;
+  p.workspace_bytes = (size_t)p.workgroups * kLayoutWaves * (size_t)(E + 1) * sizeof(int32_t);
+  return p;
+}
+
 namespace {
 
 constexpr int kThreads = kLayoutWaves * kWave;
@@ -554,11 +571,19 @@ hipError_t launch_layout(const ep_config &c, const LayoutPlan &plan, const int32
                      topk_idx, plan.P, E, plan.S, plan.C, hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  return launch_layout_scatter(c, plan, topk_idx, h, workspace, s);
+}
+
+hipError_t launch_layout_scatter(const ep_config &c, const LayoutPlan &plan,
+                                 const int32_t *topk_idx, const ep_layout_t &h, void *workspace,
+                                 hipStream_t s) {
+  const int E = c.num_experts;
   const size_t lds_scatter =
       (((size_t)(E + 1) + (size_t)kLayoutWaves * E + 8 + 3) / 4 * 4 + (size_t)kLayoutWaves * kStage) *
       sizeof(int32_t);
   hipLaunchKernelGGL(layout_scatter_kernel, dim3(plan.workgroups), dim3(kThreads), lds_scatter, s,
-                     topk_idx, plan.P, E, c.num_ranks, plan.S, plan.C, (const int32_t *)hist, h);
+                     topk_idx, plan.P, E, c.num_ranks, plan.S, plan.C,
+                     (const int32_t *)workspace, h);
   return hipGetLastError();
 }
 

@@ -331,13 +331,26 @@ __device__ inline int row_pick(bool has, uint32_t bits, int row, uint32_t &best_
   return m ? (int)__builtin_ctz(m) : -1;
 }
 
-template <int NPER>
-__global__ __launch_bounds__(kWave) void route_rows_kernel(
+// COUNT: the layout's chunk histograms come from the router itself.
+// Workgroup c (kRouteCountWaves waves) routes exactly the tokens
+// [c*tpc, c*tpc + tpc) -- the layout's chunk c -- counts the physical experts
+// it writes (entry E: indices outside [0,E), i.e. -1 for a logical expert
+// without a replica) in LDS with integer atomics, whose order does not change
+// the counts, and writes them as column c of the scatter kernel's table
+// [C/4][E+1][4]; the workgroup of the last chunk also zeroes the columns past
+// C in its group.  The routing itself is the same code, so indices and
+// weights are identical to the grid-stride launch.
+static_assert(kRouteCountStep == kRouteCountWaves * kRowTokens, "router step");
+
+template <int NPER, bool COUNT>
+__global__ __launch_bounds__(COUNT ? kWave * kRouteCountWaves : kWave) void route_rows_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias,
     const int32_t *__restrict__ rep_off, const int32_t *__restrict__ rep_slots, int32_t T,
     int32_t El, int32_t k, int32_t gate, int32_t G, int32_t TG, int32_t topn, int32_t renorm,
-    int32_t *__restrict__ idx, float *__restrict__ wout) {
-  const int lane = threadIdx.x, row = lane / kRowLanes, lr = lane % kRowLanes;
+    int32_t *__restrict__ idx, float *__restrict__ wout, int32_t E, int32_t tpc, int32_t C,
+    int32_t *__restrict__ hist) {
+  extern __shared__ int32_t cnt[];  // COUNT: [E+1] this chunk's expert histogram
+  const int lane = threadIdx.x % kWave, row = lane / kRowLanes, lr = lane % kRowLanes;
   const int e0 = lr * NPER;
   const int gs = El / G;
   const int lpg = gs / NPER;  // lanes per group (G > 1: a power of two <= 16)
@@ -347,10 +360,18 @@ __global__ __launch_bounds__(kWave) void route_rows_kernel(
 #pragma unroll
   for (int i = 0; i < NPER; ++i) valid_e |= (e0 + i < El) ? 1u << i : 0u;
 
-  for (int64_t tb = (int64_t)blockIdx.x * kRowTokens; tb < T;
-       tb += (int64_t)gridDim.x * kRowTokens) {
+  int64_t tb0 = (int64_t)blockIdx.x * kRowTokens, tend = T, tstep = (int64_t)gridDim.x * kRowTokens;
+  if (COUNT) {
+    for (int e = threadIdx.x; e <= E; e += kWave * kRouteCountWaves) cnt[e] = 0;
+    __syncthreads();
+    const int64_t c0 = (int64_t)blockIdx.x * tpc;
+    tb0 = c0 + (int64_t)(threadIdx.x / kWave) * kRowTokens;
+    tend = (c0 + tpc < T) ? c0 + tpc : T;
+    tstep = kRouteCountStep;
+  }
+  for (int64_t tb = tb0; tb < tend; tb += tstep) {
     const int64_t t = tb + row;
-    const bool live = t < T;
+    const bool live = t < tend;
     const uint32_t valid = live ? valid_e : 0u;
     const float *zr = logits + (live ? t : 0) * (int64_t)El;
     float z[NPER];
@@ -479,8 +500,68 @@ __global__ __launch_bounds__(kWave) void route_rows_kernel(
       }
       idx[t * k + lr] = phys;
       wout[t * k + lr] = ws;
+      if (COUNT) atomicAdd(&cnt[((uint32_t)phys < (uint32_t)E) ? phys : E], 1);
     }
   }
+  if (COUNT) {
+    __syncthreads();
+    const int64_t E1 = (int64_t)E + 1;
+    const int c = (int)blockIdx.x;
+    int32_t *col = hist + (int64_t)(c / kLayoutWaves) * E1 * kLayoutWaves + c % kLayoutWaves;
+    for (int e = threadIdx.x; e < E1; e += kWave * kRouteCountWaves) col[e * kLayoutWaves] = cnt[e];
+    if (c == C - 1) {
+      for (int cc = C; cc % kLayoutWaves != 0; ++cc) {
+        int32_t *z = hist + (int64_t)(cc / kLayoutWaves) * E1 * kLayoutWaves + cc % kLayoutWaves;
+        for (int e = threadIdx.x; e < E1; e += kWave * kRouteCountWaves) z[e * kLayoutWaves] = 0;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+namespace {
+
+// Experts per lane of the four-tokens-per-wave kernel, or 0 where it does not
+// apply: T >= kRowMinTokens, El <= 512, k <= 16, and groups covering
+// power-of-two runs of at most 16 lanes.
+int rows_nper(const ep_config &c, const ep_router_t &rt) {
+  const int El = rt.num_logical;
+  int nrow = 1;
+  while (nrow * kRowLanes < El) nrow *= 2;
+  const int gs = El / rt.num_groups, lpg = gs / nrow;
+  const bool rows = c.num_tokens >= kRowMinTokens && El <= kRowLanes * 32 &&
+                    c.num_topk <= kRowLanes &&
+                    (rt.num_groups == 1 ||
+                     (gs % nrow == 0 && lpg <= kRowLanes && (lpg & (lpg - 1)) == 0));
+  return rows ? nrow : 0;
+}
+
+// COUNT = false: grid-stride over the tokens, nothing counted (the plan is
+// unused); COUNT = true: one workgroup per chunk of `plan`.
+template <bool COUNT>
+hipError_t launch_rows(const ep_config &c, const ep_router_t &rt, int nrow, const float *logits,
+                       const float *bias, const int32_t *rep_off, const int32_t *rep_slots,
+                       int32_t *topk_idx, float *topk_w, const LayoutPlan &plan, int32_t *hist,
+                       hipStream_t s) {
+  const int grid = COUNT ? plan.C : row_grid(c, (c.num_tokens + kRowTokens - 1) / kRowTokens);
+  const int block = COUNT ? kWave * kRouteCountWaves : kWave;
+  const size_t lds = COUNT ? (size_t)(c.num_experts + 1) * sizeof(int32_t) : 0;
+#define EP_ROUTE_ROWS(N)                                                                         \
+  hipLaunchKernelGGL((route_rows_kernel<N, COUNT>), dim3(grid), dim3(block), lds, s, logits,     \
+                     bias, rep_off, rep_slots, c.num_tokens, rt.num_logical, c.num_topk, rt.gate, \
+                     rt.num_groups, rt.topk_groups, rt.group_topn, rt.renormalize, topk_idx,    \
+                     topk_w, c.num_experts, plan.tpc, plan.C, hist)
+  switch (nrow) {
+    case 1: EP_ROUTE_ROWS(1); break;
+    case 2: EP_ROUTE_ROWS(2); break;
+    case 4: EP_ROUTE_ROWS(4); break;
+    case 8: EP_ROUTE_ROWS(8); break;
+    case 16: EP_ROUTE_ROWS(16); break;
+    default: EP_ROUTE_ROWS(32); break;
+  }
+#undef EP_ROUTE_ROWS
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -490,30 +571,10 @@ hipError_t launch_route(const ep_config &c, const ep_router_t &rt, const float *
                         int32_t *topk_idx, float *topk_w, hipStream_t s) {
   const int El = rt.num_logical;
   // four tokens per wave where the shape allows it
-  int nrow = 1;
-  while (nrow * kRowLanes < El) nrow *= 2;
-  const int gs = El / rt.num_groups, lpg = gs / nrow;
-  const bool rows = c.num_tokens >= kRowMinTokens && El <= kRowLanes * 32 &&
-                    c.num_topk <= kRowLanes &&
-                    (rt.num_groups == 1 ||
-                     (gs % nrow == 0 && lpg <= kRowLanes && (lpg & (lpg - 1)) == 0));
-  if (rows) {
-    const int grid = row_grid(c, (c.num_tokens + kRowTokens - 1) / kRowTokens);
-#define EP_ROUTE_ROWS(N)                                                                         \
-  hipLaunchKernelGGL(route_rows_kernel<N>, dim3(grid), dim3(kWave), 0, s, logits, bias, rep_off, \
-                     rep_slots, c.num_tokens, El, c.num_topk, rt.gate, rt.num_groups,          \
-                     rt.topk_groups, rt.group_topn, rt.renormalize, topk_idx, topk_w)
-    switch (nrow) {
-      case 1: EP_ROUTE_ROWS(1); break;
-      case 2: EP_ROUTE_ROWS(2); break;
-      case 4: EP_ROUTE_ROWS(4); break;
-      case 8: EP_ROUTE_ROWS(8); break;
-      case 16: EP_ROUTE_ROWS(16); break;
-      default: EP_ROUTE_ROWS(32); break;
-    }
-#undef EP_ROUTE_ROWS
-    return hipGetLastError();
-  }
+  const int nrow = rows_nper(c, rt);
+  if (nrow > 0)
+    return launch_rows<false>(c, rt, nrow, logits, bias, rep_off, rep_slots, topk_idx, topk_w,
+                              LayoutPlan{}, nullptr, s);
   const int grid = row_grid(c, c.num_tokens);
   const size_t lds = (size_t)rt.num_logical * sizeof(float);  // scores, for the LDS group path
 #define EP_ROUTE_LAUNCH(N)                                                                     \
@@ -529,6 +590,24 @@ hipError_t launch_route(const ep_config &c, const ep_router_t &rt, const float *
   else EP_ROUTE_LAUNCH(32);
 #undef EP_ROUTE_LAUNCH
   return hipGetLastError();
+}
+
+hipError_t launch_route_layout(const ep_config &c, const ep_router_t &rt, const float *logits,
+                               const float *bias, const int32_t *rep_off,
+                               const int32_t *rep_slots, int32_t *topk_idx, float *topk_w,
+                               const ep_layout_t &h, void *workspace, hipStream_t s) {
+  const int nrow = rows_nper(c, rt);
+  const LayoutPlan fp = plan_route_count(c.num_tokens, c.num_topk, c.num_experts);
+  if (nrow == 0 || fp.C == 0 || c.num_workgroups > 0) {
+    const hipError_t err = launch_route(c, rt, logits, bias, rep_off, rep_slots, topk_idx, topk_w, s);
+    if (err != hipSuccess) return err;
+    return launch_layout(c, plan_layout((int64_t)c.num_tokens * c.num_topk, c.num_experts),
+                         topk_idx, h, workspace, s);
+  }
+  const hipError_t err = launch_rows<true>(c, rt, nrow, logits, bias, rep_off, rep_slots, topk_idx,
+                                           topk_w, fp, static_cast<int32_t *>(workspace), s);
+  if (err != hipSuccess) return err;
+  return launch_layout_scatter(c, fp, topk_idx, h, workspace, s);
 }
 
 }  // namespace ep

@@ -145,8 +145,9 @@ const char *ep_status_string(ep_status status);
  * Returns -1 for an invalid config. */
 int64_t ep_recv_capacity_rows(const ep_config *cfg /*(host)*/);
 
-/* Bytes of device workspace ep_layout needs for this config (its per-chunk
- * expert histograms).  Returns 0 for an invalid config. */
+/* Bytes of device workspace ep_layout, ep_layout_dispatch and ep_route_layout
+ * need for this config (their per-chunk expert histograms; the larger of the
+ * two table shapes).  Returns 0 for an invalid config. */
 size_t ep_layout_workspace_bytes(const ep_config *cfg /*(host)*/);
 
 /* Routing layout ([Perplexity blog] "MoE-beirari"; [DeepEP overview] "Pola
@@ -289,8 +290,8 @@ ep_status ep_silu_mul_quant(const ep_config *cfg /*(host)*/, const ep_layout_t *
  * EP_DEVERR_INDEX.  Without a table (both NULL) topk_idx holds logical ids and
  * cfg->num_experts must equal El.  Logits must be finite (otherwise the
  * choice is unspecified but still k distinct experts).  cfg->hidden and
- * num_ranks are checked as everywhere but not used.  One launch, one wave
- * per token. */
+ * num_ranks are checked as everywhere but not used.  One launch: one wave
+ * per token, or four tokens per wave from 2048 tokens on (same results). */
 ep_status ep_route(const ep_config *cfg /*(host)*/, const ep_router_t *router /*(host)*/,
                    const float *logits, const float *bias, const int32_t *replica_offsets,
                    const int32_t *replica_slots, int32_t *topk_idx, float *topk_weights,
@@ -299,7 +300,13 @@ ep_status ep_route(const ep_config *cfg /*(host)*/, const ep_router_t *router /*
 /* ep_route followed by ep_layout on its output ([Perplexity blog]
  * "MoE-beirari": the dense dispatch and combine need the routing summed per
  * expert), so the handle is built from the logits with no host round trip.
- * Arguments as for the two calls; `workspace` as for ep_layout. */
+ * Where ep_layout would take two launches and the router routes four tokens
+ * per wave (E <= 512, num_workgroups 0), the router also counts the layout's
+ * per-chunk expert histograms -- one router workgroup per chunk of tokens --
+ * so only the layout's scatter kernel follows (two launches instead of
+ * three); otherwise it runs the two calls' kernels in turn.  The results are
+ * the same bytes either way.  Arguments as for the two calls; `workspace` as
+ * for ep_layout. */
 ep_status ep_route_layout(const ep_config *cfg /*(host)*/, const ep_router_t *router /*(host)*/,
                           const float *logits, const float *bias, const int32_t *replica_offsets,
                           const int32_t *replica_slots, int32_t *topk_idx, float *topk_weights,

@@ -66,12 +66,20 @@ def test_status_strings(lib):
 def test_capacity_and_workspace(lib):
     c = ep.Config(8192, 7168, 8, 256, 8, fp8=True)
     assert ep.ep_recv_capacity_rows(c) == 8192 * 8
-    assert ep.ep_layout_workspace_bytes(c) == 128 * 257 * 4  # 128 chunks of 512 pairs
+    # ep_layout: 128 chunks of 512 pairs; ep_route_layout's router-counted
+    # table: one chunk per router workgroup of 32 tokens, 256 chunks -- the
+    # larger one is returned
+    assert ep.ep_layout_workspace_bytes(c) == 256 * 257 * 4
+    # 20000 tokens, k=3, E=512: the router-counted table has 3 router steps
+    # (96 tokens) per chunk, 209 chunks, padded to 212 columns
+    c = ep.Config(20000, 256, 3, 512, 8)
+    assert ep.ep_layout_workspace_bytes(c) == 212 * 513 * 4
     # up to 8192 pairs and 512 experts the layout is one launch: no table
     c = ep.Config(128, 7168, 8, 288, 36, fp8=True)
     assert ep.ep_layout_workspace_bytes(c) == 256
     c = ep.Config(30000, 7168, 8, 256, 8)  # 240000 pairs: chunks grow to 960 pairs so C <= 255
     assert ep.ep_layout_workspace_bytes(c) == 252 * 257 * 4  # 250 chunks in groups of 4
+    # (the router-counted table: 128-token chunks, 235 of them -> 236 columns, smaller)
     # many pairs, many experts: the chunk count is capped so the table stays small
     c = ep.Config(1 << 20, 256, 8, 2048, 8)
     ws = ep.ep_layout_workspace_bytes(c)

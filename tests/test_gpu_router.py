@@ -231,3 +231,70 @@ def test_route_layout_flags_a_missing_replica():
                        idx, wts, h, ws)
     torch.cuda.synchronize()
     assert int(h.error_flag.cpu()[0]) & ep.EP_DEVERR_INDEX
+
+
+def route_layout(T, k, E, R, z, num_workgroups=0, **kw):
+    """ep_route_layout on fresh poisoned buffers: (idx, weights, handle arrays)."""
+    from combine_ep_layout_03_amd.buffers import Handle, alloc_workspace
+    cfg = ep.Config(T, 128, k, E, R, num_workgroups=num_workgroups)
+    rt = ep.Router(z.shape[1], kw.get("gate", "sigmoid"), kw.get("n_groups", 1), kw.get("topk_groups", 1),
+                   kw.get("group_topn", 2), kw.get("renorm", True))
+    h = Handle.alloc(cfg, "cuda")
+    for t in vars(h).values():
+        t.view(torch.uint8).fill_(POISON)
+    ws = alloc_workspace(cfg, "cuda")
+    ws.fill_(0x5A)   # contents on entry must not matter
+    opt = lambda a: None if kw.get(a) is None else to_dev(kw[a])
+    idx = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    wts = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+    ep.ep_route_layout(cfg, rt, to_dev(z), opt("bias"), opt("rep_offsets"), opt("rep_slots"), idx, wts, h, ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), wts.cpu().numpy(), {n: t.cpu().numpy() for n, t in vars(h).items()}
+
+
+# Shapes of the router-counted layout (the router writes the chunk table, the
+# scatter kernel follows): one router step per chunk (2048 and 8192 tokens),
+# a one-token tail chunk with odd k, two steps per chunk (8193 tokens), three
+# steps with E = 512 and odd k, groups + bias, replicas; and the same call
+# with num_workgroups set, which takes router + two-launch layout instead.
+@pytest.mark.parametrize("T,El,k,G,TG,extra", [
+    (2048, 256, 8, 1, 1, ""), (2049, 64, 5, 1, 1, ""), (8192, 256, 8, 8, 4, "bias"),
+    (8193, 256, 8, 8, 4, ""), (20000, 512, 3, 1, 1, ""), (3000, 128, 16, 4, 2, "bias"),
+    (4100, 256, 8, 8, 4, "replicas"),
+])
+def test_route_layout_router_counted(T, El, k, G, TG, extra):
+    rng = np.random.default_rng(T + El + k)
+    z = (rng.standard_normal((T, El)) * 2).astype(np.float32)
+    kw = dict(gate="sigmoid" if T % 2 == 0 else "softmax", n_groups=G, topk_groups=TG)
+    E = El
+    if extra == "bias":
+        kw["bias"] = (rng.standard_normal(El) * 0.5).astype(np.float32)
+    if extra == "replicas":
+        n = 1 + (rng.random(El) < 0.125).astype(np.int64)
+        kw["rep_offsets"] = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        E = int(kw["rep_offsets"][-1])
+        kw["rep_slots"] = rng.permutation(E).astype(np.int32)
+    R = 8 if E % 8 == 0 else 1
+    say(f"route_layout counted T={T} El={El} k={k} E={E} R={R} G={G} TG={TG} {extra}")
+    ri, rw = oracle.route(z, k, **kw)
+    L = oracle.layout(ri, E, R)
+    for nwg in (0, 7):
+        gi, gw, h = route_layout(T, k, E, R, z, num_workgroups=nwg, **kw)
+        assert np.array_equal(gi, ri) and np.array_equal(gw.view(np.uint32), rw.view(np.uint32)), nwg
+        assert h["error_flag"][0] == 0, nwg
+        for key in ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "src_of"):
+            assert np.array_equal(h[key].reshape(-1), getattr(L, key).reshape(-1)), (nwg, key)
+        assert np.array_equal(h["slot_of"].reshape(-1), L.slot_of.reshape(-1)), nwg
+
+
+def test_route_layout_router_counted_flags_a_missing_replica():
+    # at a size where the router counts the table: the -1 picks land in the
+    # table's bad-index entry and the scatter raises EP_DEVERR_INDEX
+    El, T, k = 64, 2048, 5     # 10240 pairs: the two-launch layout's size
+    off = np.array([0, 0] + list(range(1, El)), np.int32)   # n_0 = 0, the others 1
+    slots = np.arange(El - 1, dtype=np.int32)
+    z = np.zeros((T, El), np.float32)
+    z[:, 0] = 5.0
+    gi, _, h = route_layout(T, k, El - 1, 1, z, gate="softmax", rep_offsets=off, rep_slots=slots)
+    assert np.all(gi[:, 0] == -1)
+    assert int(h["error_flag"][0]) & ep.EP_DEVERR_INDEX
