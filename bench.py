@@ -128,7 +128,8 @@ def cpu_baseline(workload_name, sample_tokens, min_seconds):
 
 
 # rocprofv3 kernel names ("ep::(anonymous namespace)::combine_kernel<false>(int const*, ...")
-# matched by anchored patterns: combine_kernel<false> is ep_combine, <true> ep_combine_shared
+# matched by anchored patterns: combine_kernel<false> is ep_combine, <true> ep_combine_shared;
+# route_rows_kernel<N, true> is the router that also counts the layout's chunk table
 KERNEL_KEYS = {
     "combine": r"::combine_kernel(<false>)?\(",
     "dispatch": r"::dispatch_(fp8|bf16)_kernel\(",
@@ -136,7 +137,8 @@ KERNEL_KEYS = {
     "layout_scatter": r"::layout_scatter_kernel\(",
     "layout_small": r"::layout_small_kernel\(",
     "layout_tiny": r"::layout_tiny_kernel\(",
-    "route": r"::route(_rows)?_kernel<\d+>\(",
+    "route": r"::(route_kernel<\d+>|route_rows_kernel<\d+, false>)\(",
+    "route_count": r"::route_rows_kernel<\d+, true>\(",
     "layout_dispatch_small": r"::layout_dispatch_small_kernel<(true|false)>\(",
     "combine_shared": r"::combine_kernel<true>\(",
     "combine_backward": r"::combine_backward_(wave|wg)_kernel\(",
