@@ -22,7 +22,9 @@
 // Decode-sized problems (P <= kFusedMaxPairs) run in ONE launch of one
 // single-wave workgroup per 64 pairs, each counting every pair itself.  Small
 // problems (P <= kSmallMaxPairs, E <= kSmallMaxExperts) run all three phases
-// in ONE launch of one 16-wave workgroup (its waves are the chunks).  Larger ones use two launches: a count kernel writes
+// in ONE launch of one or two 16-wave workgroups of ~4096 pairs (their waves
+// are the chunks), each again counting every pair itself.  Larger ones use
+// two launches: a count kernel writes
 // a [C/4][E+1][4] table of chunk histograms (a workgroup's 4 chunks are one
 // 16-byte group per expert; entry E counts bad indices) to the workspace,
 // and a scatter kernel in which every workgroup reads the whole table --
@@ -31,7 +33,9 @@
 // prefixes before walking.  (Measured at T*k = 65536: reading expert-major
 // rows, each instruction touching 64 lines, cost 5.8 us of a 15 us scatter
 // kernel; making every workgroup of one launch count all pairs itself costs
-// more in LDS atomics than the second launch.)
+// more in LDS atomics than the second launch.)  In ep_route_layout the router
+// writes that table itself (plan_route_count: one router workgroup per
+// chunk), and only the scatter kernel runs here.
 #include "ep_device.h"
 #include "ep_internal.h"
 

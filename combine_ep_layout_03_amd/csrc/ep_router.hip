@@ -24,7 +24,10 @@
 // score group c.  Renormalization sums the k picks in order with readlane, so
 // the weights are the same binary32 operations as a sequential loop.  fp
 // contraction is off: the scores are exact compositions of correctly rounded
-// operations.
+// operations.  Large batches take a second kernel that routes four tokens
+// per wave (same results); in ep_route_layout it also counts the layout's
+// per-chunk expert histograms, one workgroup per chunk, so the layout's
+// count launch is not needed.
 #include <math.h>
 
 #include "ep_device.h"
