@@ -12,7 +12,8 @@ The bar is the usual one: layout and dispatch bytes exact, combine within
 Two more sweeps draw random router configurations (gate, groups, kept
 groups, group score form, bias, replicas; both router kernels by batch size)
 checked bit for bit, and random shapes through the shared-expert combine,
-both combine-backward paths and the SiLU re-quantization.
+both combine-backward paths and the SiLU re-quantization.  A last sweep draws
+ep_route_layout shapes on which the router counts the layout's chunk table.
 """
 import numpy as np
 import pytest
@@ -179,3 +180,43 @@ def test_random_shared_backward_and_silu(seed):
         dec = oracle.e4m3_decode(q).astype(np.float64) * sg
         bound = np.maximum(2.0 ** -4 * np.abs(ar), 2.0 ** -10 * sg) * (1 + 1e-5) + 1e-6 * (np.abs(ar) + sg)
         assert np.all(np.abs(dec - ar) <= bound), r
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_route_layout(seed):
+    """Random shapes for ep_route_layout where the router counts the layout's
+    chunk table (T >= 2048, two-launch layout sizes, E <= 512): indices and
+    weights bit for bit against the oracle's router, the handle against the
+    oracle's layout, and the same bytes with num_workgroups set (router, then
+    the two-launch layout)."""
+    from test_gpu_router import route_layout
+    rng = np.random.default_rng(4000 + seed)
+    G = int(rng.choice([1, 1, 2, 4, 8]))
+    El = int(rng.choice([64, 128, 256, 512]))
+    gs = El // G
+    TG = int(rng.integers(1, G + 1))
+    k = int(rng.integers(2, min(TG * gs, 16) + 1))
+    T = int(rng.integers(2048, 12001))
+    z = (rng.standard_normal((T, El)) * float(rng.choice([0.5, 2, 8]))).astype(np.float32)
+    kw = dict(gate=["softmax", "sigmoid"][seed % 2], n_groups=G, topk_groups=TG,
+              group_topn=int(rng.integers(1, 3)), renorm=bool(rng.integers(0, 2)))
+    if rng.integers(0, 2):
+        kw["bias"] = (rng.standard_normal(El) * 0.5).astype(np.float32)
+    E = El
+    if El <= 256 and rng.integers(0, 2):
+        n = 1 + (rng.random(El) < 0.25).astype(np.int64)
+        kw["rep_offsets"] = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        E = int(kw["rep_offsets"][-1])
+        kw["rep_slots"] = rng.permutation(E).astype(np.int32)
+    R = int(rng.choice([r for r in (1, 2, 4, 8, 16) if E % r == 0]))
+    say(f"random route_layout {seed}: T={T} El={El} k={k} E={E} R={R} G={G} TG={TG} "
+        f"topn={kw['group_topn']} bias={'bias' in kw}")
+    ri, rw = oracle.route(z, k, **kw)
+    L = oracle.layout(ri, E, R)
+    for nwg in (0, 5):
+        gi, gw, h = route_layout(T, k, E, R, z, num_workgroups=nwg, **kw)
+        assert np.array_equal(gi, ri) and np.array_equal(gw.view(np.uint32), rw.view(np.uint32)), nwg
+        assert h["error_flag"][0] == 0, nwg
+        for key in ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "src_of"):
+            assert np.array_equal(h[key].reshape(-1), getattr(L, key).reshape(-1)), (nwg, key)
+        assert np.array_equal(h["slot_of"].reshape(-1), L.slot_of.reshape(-1)), nwg
