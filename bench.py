@@ -75,7 +75,9 @@ def source_sha(paths):
 
 def kernel_sources():
     c = os.path.join(ROOT, "combine_ep_layout_03_amd", "csrc")
-    common = [os.path.join(c, "ep_internal.h"), os.path.join(c, "ep_device.h")]
+    # the kernels' own file plus the headers whose constants and helpers they use
+    common = [os.path.join(c, "ep_internal.h"), os.path.join(c, "ep_device.h"),
+              os.path.join(ROOT, "include", "ep.h")]
     return {"combine": [os.path.join(c, "ep_combine.hip")] + common,
             "dispatch": [os.path.join(c, "ep_dispatch.hip")] + common}
 

@@ -47,8 +47,10 @@
  *   - Host-checkable problems (NULL pointers, bad sizes, too small a
  *     capacity) return a nonzero ep_status at once and enqueue nothing.
  *   - Data problems found on the device (a routing index outside [0,E), a
- *     row outside the capacity) set bits in the handle's error word; dispatch,
- *     combine and unpermute read the word first and then write nothing.
+ *     row outside the capacity) set bits in the handle's error word; every
+ *     call that reads a handle (dispatch, combine with or without the shared
+ *     expert, combine backward, the SiLU re-quantization, unpermute) reads
+ *     the word first and then writes nothing.
  *   - Output bytes do not depend on ep_config.num_workgroups.
  *
  * Data types: routing indices int32 [T,k] row-major; weights fp32 [T,k];
@@ -104,8 +106,12 @@ typedef struct {
   int32_t num_ranks;      /* R in [1, EP_MAX_RANKS] */
   int32_t dispatch_dtype; /* ep_dtype (cf. use_fp8_dispatch) */
   int32_t num_workgroups; /* 0 = analytic default; otherwise the grid size of
-                             dispatch / combine / unpermute (cf. the per-call
-                             SM-count override) */
+                             the per-row kernels: dispatch, combine (and with
+                             the shared expert), combine backward, unpermute,
+                             the SiLU re-quantization, the router and the
+                             one-launch layout + dispatch (cf. the per-call
+                             SM-count override).  The layout's kernels keep
+                             their own grids. */
 } ep_config;
 
 /* The routing handle.  Caller-allocated device arrays; ep_layout fills them
