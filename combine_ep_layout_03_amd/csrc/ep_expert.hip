@@ -13,12 +13,12 @@
 // kernel reads on the device (a binary search per work unit), so the launch
 // needs no host copy of the counts and can be captured in a graph.  A unit is
 // (slot, segment of 8 blocks of 128 channels); a lane holds 16 channels of
-// gate and up, computes a = g * rcp(1 + e^-g) * u in binary32 (the device
-// expf and the 1-ulp hardware reciprocal: the activation is specified to a
-// tolerance against a binary64 reference, and the correctly rounded divide
-// made this ALU-bound), then the block amax and the correctly rounded scale
-// as dispatch does, and codes of a * (1/s) with one divide per block (within
-// 1.5 binary32 ulps of a/s, inside the same tolerance).
+// gate and up, computes a = g * rcp(1 + e^-g) * u in binary32 (exp_neg below
+// and the 1-ulp hardware reciprocal: the activation is specified to a
+// tolerance against a binary64 reference, and the kernel is bound by its
+// VALU work as much as by memory), then the block amax and the correctly
+// rounded scale as dispatch does, and codes of a * (1/s) with one divide per
+// block (within 1.5 binary32 ulps of a/s, inside the same tolerance).
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -28,6 +28,29 @@ namespace {
 using namespace dev;
 
 constexpr int kSegBlocks = 8;
+
+// e^-g for the activation.  With x = -g, e^x = 2^(x log2 e) is taken on the
+// hardware base-2 exponential with the argument reduction of the
+// split-constant method: log2(e) = C_hi + C_lo (C_hi its binary32 rounding),
+// t = RN(x * C_hi), and d = x*C_hi - t + x*C_lo recovered with two fused
+// multiply-adds (the product's rounding error is exact in an fma), so
+// e^x = 2^t * 2^d ~ 2^t * (1 + d ln 2).  Wherever 2^t is finite (|t| < 128)
+// |d| < 2^-16, so the neglected (d ln 2)^2 / 2 is below 2^-33.  x is clamped
+// to [-200, 200] first, beyond which 2^t is already 0 or +inf in binary32, so
+// every special input gives what e^x gives; a NaN gate stays a NaN in the
+// activation through the factor g.  Measured over every bf16 gate
+// value: the activation is within 2.34 binary32 ulps of binary64 (2.25 with
+// the device expf), with the same NaN / inf outputs; it takes about 110
+// fewer VALU instructions per wave than expf.
+__device__ inline float exp_neg(float g) {
+  const float x = __builtin_amdgcn_fmed3f(-g, -200.0f, 200.0f);
+  const float c_hi = 1.44269502162933349609375f;    // binary32 nearest log2(e)
+  const float c_lo = 1.925963033500011e-08f;        // log2(e) - c_hi
+  const float ln2 = 0.693147182464599609375f;       // binary32 nearest ln 2
+  const float t = x * c_hi;
+  const float d = __builtin_fmaf(x, c_lo, __builtin_fmaf(x, c_hi, -t));
+  return __builtin_amdgcn_exp2f(t) * __builtin_fmaf(d, ln2, 1.0f);
+}
 
 __global__ __launch_bounds__(kWave) void silu_mul_quant_kernel(
     const int32_t *__restrict__ rank_offsets, const int32_t *__restrict__ err, int64_t P,
@@ -67,8 +90,8 @@ __global__ __launch_bounds__(kWave) void silu_mul_quant_kernel(
       const uint32_t gw = gv[i % 4], uw = uv[i % 4];
       const float ga = __uint_as_float(gw << 16), gb = __uint_as_float(gw & 0xFFFF0000u);
       const float ua = __uint_as_float(uw << 16), ub = __uint_as_float(uw & 0xFFFF0000u);
-      a[2 * i] = ga * __builtin_amdgcn_rcpf(1.0f + expf(-ga)) * ua;
-      a[2 * i + 1] = gb * __builtin_amdgcn_rcpf(1.0f + expf(-gb)) * ub;
+      a[2 * i] = ga * __builtin_amdgcn_rcpf(1.0f + exp_neg(ga)) * ua;
+      a[2 * i + 1] = gb * __builtin_amdgcn_rcpf(1.0f + exp_neg(gb)) * ub;
     }
     float s;
     const u32x4 q = quant_block16_f32(a, s);

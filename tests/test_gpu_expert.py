@@ -2,7 +2,8 @@
 re-quantization on the received rows) against the oracle.
 
 The oracle's activation is binary64 rounded once to fp32; the kernel's is
-binary32 with the device expf, within a few fp32 ulps of it.  So the bar is:
+binary32 (an exp2-based exponential and the hardware reciprocal), within a
+few fp32 ulps of it.  So the bar is:
 scales within a relative 1e-6; every code's dequantized value within the
 E4M3 half-ulp bound of the oracle's activation, max(2^-4 |a|, 2^-10 s), plus
 1e-6 of slack for that activation error; and (reported) almost every code
@@ -30,10 +31,18 @@ def gpu_ready():
 
 def check_silu(name, T, I, scale=1.5, seed=0):
     w = make_workload(name, T=T)
-    run = GpuRun(w).layout()
-    L = oracle.layout(w.topk_idx, w.E, w.R)
     rng = np.random.default_rng(seed)
     act = bf16_from_f32((rng.standard_normal((w.P, 2 * I)) * scale).astype(np.float32))
+    check_silu_act(w, I, act)
+
+
+def check_silu_act(w, I, act, name=None):
+    """ep_silu_mul_quant on act [T*k, 2I] bf16 (rows in slot order) against
+    the oracle: scales within 1e-6, codes within the E4M3 bound of the
+    oracle's binary64 activation, >= 99.9 % identical codes."""
+    name = name or w.name
+    run = GpuRun(w).layout()
+    L = oracle.layout(w.topk_idx, w.E, w.R)
     act_r = [act[L.rank_offsets[r]:L.rank_offsets[r + 1]] for r in range(w.R)]
     ins = rows_to_dev(run.cap, 2 * I, act_r)
     qs = [torch.full((run.cap, I), POISON, dtype=torch.uint8, device="cuda") for _ in range(w.R)]
@@ -78,3 +87,23 @@ def test_silu_mul_quant_wide_range():
 
 def test_silu_mul_quant_full_headline():
     check_silu("v3", None, 2048)
+
+
+def test_silu_mul_quant_every_bf16_gate_value():
+    # every finite bf16 pattern as a gate (up = 1), ordered by |gate| so each
+    # 128-channel block spans a narrow range of magnitudes: exercises the
+    # activation's exponential over its whole input range (saturation,
+    # underflow, signed zeros, subnormal gates) through the public call
+    w = make_workload("tiny")              # 256 received rows
+    I = 2048
+    pats = np.arange(65536, dtype=np.uint32)
+    g = pats[((pats >> 7) & 0xFF) != 0xFF].astype(np.uint16)   # 65 280 finite values
+    gv = oracle.bf16_to_f32(g).astype(np.float64)
+    g = g[np.argsort(np.abs(gv), kind="stable")]
+    assert w.P * I >= g.size
+    gate = np.zeros(w.P * I, np.uint16)
+    gate[:g.size] = g
+    act = np.empty((w.P, 2 * I), np.uint16)
+    act[:, :I] = gate.reshape(w.P, I)
+    act[:, I:] = 0x3F80                     # bf16 1.0
+    check_silu_act(w, I, act, name="every bf16 gate")
