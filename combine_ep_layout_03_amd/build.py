@@ -34,15 +34,39 @@ def sources() -> list[str]:
     return [os.path.join(CSRC, s) for s in SOURCES]
 
 
+EXAMPLE_SRC = os.path.join(ROOT, "examples", "ep_c_example.c")
+EXAMPLE = os.path.join(ROOT, "examples", "ep_c_example")
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source into libep.so (always rebuilds).  Returns the path."""
+    """Compile every source into libep.so (always rebuilds), then the plain-C
+    example program against it.  Returns the library's path."""
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-shared", *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_example(verbose)
     return LIB
+
+
+def build_example(verbose: bool = False) -> str:
+    """The C example (examples/ep_c_example.c): gcc, C11, linked to libep.so
+    and the HIP runtime, found at run time through rpath."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cc = os.environ.get("CC") or shutil.which("gcc") or "cc"
+    tmp = EXAMPLE + ".tmp%d" % os.getpid()
+    cmd = [cc, "-O2", "-std=c11", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+           "-I", os.path.join(rocm, "include"), EXAMPLE_SRC, "-L", PKG, "-lep",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../combine_ep_layout_03_amd", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, EXAMPLE)
+    return EXAMPLE
 
 
 def is_stale() -> bool:
