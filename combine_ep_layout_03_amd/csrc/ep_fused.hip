@@ -68,10 +68,15 @@ __global__ __launch_bounds__(kWave) void layout_dispatch_small_kernel(
   const int nseg = FP8 ? (nb + kFp8SegBlocks - 1) / kFp8SegBlocks : (nch + kWave - 1) / kWave;
   const int64_t units = (int64_t)T * nseg;
 
-  // the first unit's payload, loaded now so that it overlaps the layout work
+  // the first unit's payload and its token's k indices, loaded now so that
+  // they overlap the layout work
   int64_t u = blockIdx.x;
   u32x4 pv0, pv1;
-  if (u < units) load_payload<FP8>(x, u / nseg, (int)(u % nseg), H, lane, pv0, pv1);
+  int32_t e_first = 0;
+  if (u < units) {
+    load_payload<FP8>(x, u / nseg, (int)(u % nseg), H, lane, pv0, pv1);
+    if (lane < k) e_first = idx[(u / nseg) * k + lane];
+  }
 
   // every index, coalesced: value i of this lane is pair i*64 + lane
   int32_t ev[kPL];
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(kWave) void layout_dispatch_small_kernel(
     // indices (two counts per 32-bit word, each < P <= 2048, reduced by DPP
     // row sums), plus the token's own earlier pairs with e
     const int32_t tk = (int32_t)(t * k);
-    const int32_t my_e = (lane < k) ? idx[tk + lane] : 0;
+    const int32_t my_e = (u == (int64_t)blockIdx.x) ? e_first : ((lane < k) ? idx[tk + lane] : 0);
     int32_t my_slot = 0;
     for (int j0 = 0; j0 < k; j0 += 8) {
       int32_t ej[8];
