@@ -16,8 +16,9 @@
 // token's k pairs it finds each pair's rank among the earlier pairs of the
 // same expert by counting matches in the register-held index array -- eight
 // pairs at once, two counts per word, reduced by DPP row sums -- which gives
-// exactly the stable slot of the two-pass layout.  The unit's payload is
-// loaded first, so its latency overlaps the layout work.  Segment-0 units
+// exactly the stable slot of the two-pass layout.  The unit's payload and its
+// token's k indices are loaded first, so their latency overlaps the layout
+// work (reading the indices after the histogram's barriers cost 1.3 us).  Segment-0 units
 // write their token's slot_of / src_of entries; unit 0 writes the per-expert
 // and per-rank arrays and the error word.  The row payload is the same code
 // as ep_dispatch.  (Measured on MI355X at 128 tokens x 8: counting one pair
