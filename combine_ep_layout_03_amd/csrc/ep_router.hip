@@ -1,5 +1,6 @@
 // ep_router.hip -- the MoE router on gfx950: gate scores, group-limited
-// top-k, weights and the redundant-expert mapping, one wave per token.
+// top-k, weights and the redundant-expert mapping; one wave per token, or
+// four tokens per wave for large batches.
 //
 // Pages: [Perplexity blog] "Lower latency and higher throughput with multi-
 // node DeepSeek deployment", "MoE-beirari" (one router for every MoE model:
