@@ -6,7 +6,8 @@ times with eager work (output poisoning, synchronization) between replays;
 every replay must reproduce the eager run's bytes exactly.  The workloads
 take the one-launch layout (decode), the two-launch layout with FP8 (a
 2048-token V3-shaped batch) and BF16 (DeepSeek-16B-like), and both
-combine-backward paths.
+combine-backward paths.  The same steps of three workloads also run at the
+same time on three streams and must give the bytes of a sequential run.
 """
 import numpy as np
 import pytest
@@ -134,3 +135,36 @@ def test_decode_step_in_a_graph(name, T):
     w = make_workload(name, T=T)
     say(f"graph: decode step {name} T={w.T} P={w.P}")
     run_graph(Step(w), Step.decode)
+
+
+@pytest.mark.parametrize("body", ["layer", "decode"])
+def test_independent_calls_on_concurrent_streams(body):
+    """The library keeps no state between calls: three workloads' steps run
+    at the same time on three streams (default priority) give the bytes of
+    the same steps run one after another."""
+    steps = [Step(make_workload("decode")), Step(make_workload("v3", T=2048)),
+             Step(make_workload("ds16b", T=1024))]
+    fn = getattr(Step, body)
+    cur = torch.cuda.current_stream()
+    ref = []
+    for st in steps:
+        st.poison()
+        fn(st, cur)
+        ref.append(st.snapshot())
+    say(f"concurrent streams: {body} x {len(steps)}")
+    for rep in range(3):
+        for st in steps:
+            st.poison()
+        streams = [torch.cuda.Stream() for _ in steps]
+        for st, s in zip(steps, streams):
+            s.wait_stream(cur)
+            with torch.cuda.stream(s):
+                fn(st, s)
+        for s in streams:
+            cur.wait_stream(s)
+        torch.cuda.synchronize()
+        for i, st in enumerate(steps):
+            got, counts = st.snapshot()
+            assert np.array_equal(counts, ref[i][1]), (rep, i)
+            for j, (a, b) in enumerate(zip(got, ref[i][0])):
+                assert np.array_equal(a, b), (rep, i, j)
