@@ -13,6 +13,8 @@ Prints ONE JSON line (rank 0, N=1):
   roofline     = the dominant kernel (combine): algorithmic bytes per launch /
                  its mean HIP-event duration, against 8 TB/s HBM peak
   cpu_baseline = the CPU oracle (single thread) on a bounded sample
+  cache_flushed = layout / dispatch / combine medians with a 1 GiB read
+                 before each step (cold caches), beside the back-to-back ones
   extras       = the other entry points timed in the same run (router, decode-
                  style steps, shared-expert combine, combine backward, SiLU
                  re-quantization); --no-extras skips them
@@ -366,6 +368,28 @@ def main():
         s = sorted(v)
         return round(s[min(len(s) - 1, int(q * len(s)))], 2)
 
+    # The same three calls with cold caches: before each step a 1 GiB read
+    # (4x the 256 MB MALL, 32x the L2; a read, so it leaves no dirty lines
+    # whose write-back would land in the timed kernels) runs outside the
+    # kernel events.  The timed loop above is back-to-back steps, as in a
+    # layer loop that reuses its buffers.
+    flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(min(K, 20))]
+    for e in fev:
+        flush_buf.view(torch.int64).sum()
+        e[0].record(stream)
+        layout()
+        e[1].record(stream)
+        dispatch()
+        e[2].record(stream)
+        combine()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    del flush_buf
+    assert int(h.error_flag.item()) == 0
+    flushed = {name: round(statistics.median(e[a].elapsed_time(e[a + 1]) * 1e3 for e in fev), 2)
+               for a, name in enumerate(("layout_us", "dispatch_us", "combine_us"))}
+
     extras = None
     if not args.no_extras:
         # the other entry points on the same handle and buffers: combine with a
@@ -560,6 +584,7 @@ def main():
         "dc_GBps": round((b["dispatch"] + b["combine"]) / (statistics.median(dc) * 1e-6) / 1e9, 1),
         "dispatch_GBps": round(b["dispatch"] / (statistics.median(dis) * 1e-6) / 1e9, 1),
         "combine_GBps": round(b["combine"] / (statistics.median(com) * 1e-6) / 1e9, 1),
+        "cache_flushed": flushed,
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "write_ceiling_GBps": round(write_gbps, 1),
         "bytes_per_step": step_bytes,
