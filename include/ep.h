@@ -181,7 +181,12 @@ ep_status ep_layout(const ep_config *cfg /*(host)*/, const int32_t *topk_idx,
  *   BF16: recv_x[r] row `row` (H bf16) := x[t], bit for bit;
  *   FP8:  for each 128-channel block b of x[t]: a = max|x|, s = a/448 (fp32,
  *         correctly rounded), q = E4M3(x/s) (fp32 quotient, round to nearest
- *         even, saturating at 448); a = 0 gives s = 0 and q = 0x00;
+ *         even, saturating at 448); a = 0 gives s = 0 and q = 0x00; with
+ *         non-finite values the same formulas in IEEE arithmetic: a NaN in
+ *         the block makes a and s NaN and every code NaN, an infinity makes
+ *         s = +inf (finite values -> signed zero codes, infinities -> NaN
+ *         codes); the sign and payload of NaN codes and scales are
+ *         unspecified;
  *         recv_x[r] row `row` (H bytes) := q, recv_scales[r] row `row`
  *         (H/128 fp32) := s.  Every copy of a token is byte-identical.
  * x is [T,H] bf16; recv_x / recv_scales are (host) arrays of R device

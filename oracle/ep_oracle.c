@@ -18,6 +18,9 @@
  *  - FP8 is OCP E4M3 "fn"; the per-block scale is s = a/448 rounded to binary32,
  *    the code is E4M3(RN32(x/s)) with ties to even and saturation at +-448;
  *    an all-zero block gives s = 0 and codes 0x00; signed zeros keep their sign;
+ *    non-finite values follow IEEE binary32: a NaN in a block makes its amax
+ *    (and so s and every code) NaN, an infinity makes s = +inf, so finite
+ *    values encode as signed zeros and infinities as NaN codes;
  *  - combine accumulates in binary32 with fmaf in ascending j from +0, then
  *    rounds once to bf16 with ties to even.
  */
@@ -213,10 +216,10 @@ void oracle_quantize_row(int H, const uint16_t *xrow, uint8_t *q, float *s)
 {
     for (int b = 0; b < H / 128; ++b) {
         const uint16_t *xb = xrow + b * 128;
-        float a = 0.0f; /* amax of the block */
+        float a = 0.0f; /* amax of the block; a NaN value makes it NaN */
         for (int h = 0; h < 128; ++h) {
             float v = fabsf(oracle_bf16_to_f32(xb[h]));
-            if (v > a)
+            if (v > a || isnan(v))
                 a = v;
         }
         if (a == 0.0f) {
@@ -374,10 +377,10 @@ void oracle_quantize_f32_row(int n, const float *a, uint8_t *q, float *s)
     /* the same steps as oracle_quantize_row, on binary32 activations */
     for (int b = 0; b < n / 128; ++b) {
         const float *ab = a + b * 128;
-        float amax = 0.0f;
+        float amax = 0.0f; /* a NaN value makes it NaN */
         for (int h = 0; h < 128; ++h) {
             float v = fabsf(ab[h]);
-            if (v > amax)
+            if (v > amax || isnan(v))
                 amax = v;
         }
         if (amax == 0.0f) {

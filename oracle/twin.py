@@ -23,6 +23,7 @@ rounded once.
 """
 from __future__ import annotations
 
+import math
 import struct
 from fractions import Fraction
 
@@ -97,8 +98,10 @@ _POS_CODES = [c for c in range(0x7F)]          # 0x00 .. 0x7E: every finite magn
 def e4m3_encode(v: float) -> int:
     """Nearest finite E4M3 code by brute force over the 127 magnitudes, ties
     to the code with an even mantissa; beyond 448 the code of 448; the sign
-    of zero is kept."""
+    of zero is kept; a NaN gives the NaN code S.1111.111."""
     sign = 0x80 if (f32_bits(v) >> 31) else 0
+    if v != v:
+        return sign | 0x7F
     a = abs(v)
     best = 0
     for c in _POS_CODES:
@@ -152,21 +155,31 @@ def dispatch_bf16(x, topk_idx, E, R, L):
     return recv
 
 
+def _ieee_div(x: float, y: float) -> float:
+    """x / y with IEEE results for the operands Python leaves to exceptions
+    or does not reach here (y is never 0: an all-zero block is handled
+    before)."""
+    if x != x or y != y or (math.isinf(x) and math.isinf(y)):
+        return math.nan
+    return x / y
+
+
 def quantize_row(row):
     """One token row of bf16 bits -> (codes, scales): per 128 channels
-    a = max|x|, s = a/448 in binary32, code = E4M3(binary32 x/s); a = 0 gives
-    s = 0 and codes 0."""
+    a = max|x| (NaN if the block holds a NaN), s = a/448 in binary32, code =
+    E4M3(binary32 x/s) with IEEE division (x/inf = 0, inf/inf = NaN); a = 0
+    gives s = 0 and codes 0."""
     codes, scales = [], []
     for b0 in range(0, len(row), 128):
         vals = [bf16_to_f32(v) for v in row[b0:b0 + 128]]
-        a = max(abs(v) for v in vals)
+        a = math.nan if any(v != v for v in vals) else max(abs(v) for v in vals)
         if a == 0:
             scales.append(0.0)
             codes.extend([0] * len(vals))
             continue
         s = f32(a / 448.0)
         scales.append(s)
-        codes.extend(e4m3_encode(f32(v / s)) for v in vals)
+        codes.extend(e4m3_encode(f32(_ieee_div(v, s))) for v in vals)
     return codes, scales
 
 

@@ -107,3 +107,46 @@ def test_silu_mul_quant_every_bf16_gate_value():
     act[:, :I] = gate.reshape(w.P, I)
     act[:, I:] = 0x3F80                     # bf16 1.0
     check_silu_act(w, I, act, name="every bf16 gate")
+
+
+def test_silu_mul_quant_of_nonfinite_gates():
+    """Gates +inf (activation +-inf), -inf and NaN (activation NaN) among
+    finite ones: blocks with a non-finite activation follow the IEEE reading
+    of the quantizer (R29) -- NaN scale and NaN codes for a NaN, inf scale
+    for an inf with signed zeros and NaN codes -- compared NaN against NaN;
+    the other blocks meet the usual bar."""
+    from test_gpu_parity import nan_equal_codes, nan_equal_f32
+    w = make_workload("tiny")
+    I = 512
+    rng = np.random.default_rng(8)
+    gate = (rng.standard_normal((w.P, I)) * 2).astype(np.float32)
+    up = rng.standard_normal((w.P, I)).astype(np.float32)
+    gate[rng.random((w.P, I)) < 0.001] = np.inf
+    gate[rng.random((w.P, I)) < 0.001] = -np.inf
+    gate[rng.random((w.P, I)) < 0.001] = np.nan
+    act = bf16_from_f32(np.concatenate([gate, up], axis=1))
+    run = GpuRun(w).layout()
+    L = oracle.layout(w.topk_idx, w.E, w.R)
+    act_r = [act[L.rank_offsets[r]:L.rank_offsets[r + 1]] for r in range(w.R)]
+    qs = [torch.full((run.cap, I), POISON, dtype=torch.uint8, device="cuda") for _ in range(w.R)]
+    ss = [torch.full((run.cap, I // 128), 0.5, dtype=torch.float32, device="cuda") for _ in range(w.R)]
+    say(f"silu_mul_quant of non-finite gates rows={w.P} I={I}")
+    ep.ep_silu_mul_quant(run.cfg, run.h, I, rows_to_dev(run.cap, 2 * I, act_r), qs, ss, run.cap)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.silu_mul_quant(act)
+    a_ref = oracle.silu_mul(act).astype(np.float64)
+    assert np.isnan(s_ref).any() and np.isinf(s_ref).any()
+    for r in range(w.R):
+        n, lo = int(L.rank_counts[r]), int(L.rank_offsets[r])
+        q, s = qs[r].cpu().numpy()[:n], ss[r].cpu().numpy()[:n]
+        qr, sr, ar = q_ref[lo:lo + n], s_ref[lo:lo + n], a_ref[lo:lo + n]
+        bad = ~np.isfinite(sr)                               # blocks with a non-finite activation
+        assert nan_equal_f32(s[bad], sr[bad]), r
+        qb, qrb = q.reshape(n, -1, 128), qr.reshape(n, -1, 128)
+        assert nan_equal_codes(qb[bad], qrb[bad]), r
+        good = ~bad
+        sg = np.repeat(s.astype(np.float64), 128, axis=1).reshape(n, -1, 128)[good]
+        dec = oracle.e4m3_decode(qb[good]).astype(np.float64) * sg
+        arg = ar.reshape(n, -1, 128)[good]
+        bound = np.maximum(2.0 ** -4 * np.abs(arg), 2.0 ** -10 * sg) * (1 + 1e-5) + 1e-6 * (np.abs(arg) + sg)
+        assert np.all(np.abs(dec - arg) <= bound), r
