@@ -563,9 +563,9 @@ hipError_t launch_layout(const ep_config &c, const LayoutPlan &plan, const int32
     return hipGetLastError();
   }
   if (plan.small) {
-    const size_t lds = (((size_t)(kSmallWaves + 2) * E + 1 + 2 * kSmallWaves + 3) / 4 * 4 +
-                        (size_t)kSmallWaves * kSmallStage) * sizeof(int32_t);
-    hipLaunchKernelGGL(layout_small_kernel, dim3(plan.workgroups), dim3(kSmallThreads), lds, s,
+    const size_t lds_bytes = (((size_t)(kSmallWaves + 2) * E + 1 + 2 * kSmallWaves + 3) / 4 * 4 +
+                              (size_t)kSmallWaves * kSmallStage) * sizeof(int32_t);
+    hipLaunchKernelGGL(layout_small_kernel, dim3(plan.workgroups), dim3(kSmallThreads), lds_bytes, s,
                        topk_idx, plan.P, E, c.num_ranks, plan.S, h);
     return hipGetLastError();
   }
