@@ -194,3 +194,19 @@ def test_binding_fails_loudly_without_library(tmp_path):
             _lib.load(missing)
     finally:
         _lib._lib = saved
+
+
+def test_header_is_plain_c():
+    """include/ep.h is a C header: the C example compiles as C11 with every
+    warning an error (syntax only: no library or GPU needed)."""
+    import shutil
+    gcc = shutil.which("gcc")
+    rocm_inc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")
+    if not gcc or not os.path.isdir(rocm_inc):
+        pytest.skip("gcc or the HIP headers are not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([gcc, "-std=c11", "-fsyntax-only", "-Wall", "-Wextra", "-Werror",
+                        "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"), "-I", rocm_inc,
+                        os.path.join(root, "examples", "ep_c_example.c")],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
