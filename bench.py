@@ -16,8 +16,8 @@ Prints ONE JSON line (rank 0, N=1):
   cache_flushed = layout / dispatch / combine medians with a 1 GiB read
                  before each step (cold caches), beside the back-to-back ones
   extras       = the other entry points timed in the same run (router, decode-
-                 style steps, shared-expert combine, combine backward, SiLU
-                 re-quantization); --no-extras skips them
+                 style steps, steps from the logits, shared-expert combine,
+                 combine backward, SiLU re-quantization); --no-extras skips them
 --summarize writes the profiles/ summaries from rocprofv3 CSV output.
 """
 from __future__ import annotations
@@ -507,6 +507,11 @@ def main():
         rd = lambda: L.ep_dispatch(pc, ph2, idx2.data_ptr(), x.data_ptr(), rx, rs, cap, sp)
         rc = lambda: L.ep_combine(pc, ph2, idx2.data_ptr(), ry, w2.data_ptr(), out.data_ptr(), cap, sp)
         extras["routed_step_us"] = round(step_time([rlcall, rd, rc]), 2)
+        # from the logits through the one-call layout + dispatch (one launch
+        # at decode sizes): route, layout_dispatch, combine
+        rld = lambda: L.ep_layout_dispatch(pc, idx2.data_ptr(), ph2, ws2.data_ptr(), x.data_ptr(), rx,
+                                           rs, cap, sp)
+        extras["routed_fused_step_us"] = round(step_time([rcall, rld, rc]), 2)
         assert int(h2.error_flag.item()) == 0
         assert int(h.error_flag.item()) == 0
 
