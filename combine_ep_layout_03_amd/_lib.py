@@ -168,6 +168,29 @@ def _ptrs(ts) -> ctypes.Array:
     return (ctypes.c_void_p * len(ts))(*[_ptr(t) for t in ts])
 
 
+def _need(t, nbytes: int, what: str) -> None:
+    """A tensor argument must hold at least `nbytes` bytes (raw integer
+    pointers are passed through unchecked).  The library checks NULL pointers,
+    alignment and sizes it can see; it cannot see a buffer's length."""
+    if t is None or isinstance(t, int):
+        return
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError("%s holds %d bytes, needs %d" % (what, have, nbytes))
+
+
+def _need_rows(ts, rows: int, row_bytes: int, what: str) -> None:
+    if ts is None:
+        return
+    for r, t in enumerate(ts):
+        _need(t, rows * row_bytes, "%s[%d]" % (what, r))
+
+
+def _row_bytes(c: "ep_config") -> int:
+    """Bytes of one received row: H E4M3 codes under FP8, else H bf16."""
+    return c.hidden if c.dispatch_dtype == EP_DTYPE_FP8_E4M3 else 2 * c.hidden
+
+
 def _check(status: int, what: str) -> None:
     if status != EP_OK:
         raise EpError(status, what)
@@ -200,7 +223,22 @@ def ep_layout(cfg, topk_idx, handle, workspace, stream=None) -> None:
                             _ptr(workspace), _stream(stream)), "ep_layout")
 
 
+def _check_dispatch_buffers(c, x, recv_x, recv_scales, capacity_rows) -> None:
+    _need(x, c.num_tokens * c.hidden * 2, "x")
+    _need_rows(recv_x, capacity_rows, _row_bytes(c), "recv_x")
+    if c.dispatch_dtype == EP_DTYPE_FP8_E4M3:
+        _need_rows(recv_scales, capacity_rows, 4 * (c.hidden // 128), "recv_scales")
+
+
+def _check_combine_buffers(c, recv_y, topk_weights, out, capacity_rows, out_rows=None) -> None:
+    _need_rows(recv_y, capacity_rows, 2 * c.hidden, "recv_y")
+    _need(topk_weights, c.num_tokens * c.num_topk * 4, "topk_weights")
+    rows = c.num_tokens if out_rows is None else out_rows
+    _need(out, rows * c.hidden * 2, "out")
+
+
 def ep_dispatch(cfg, handle, topk_idx, x, recv_x, recv_scales, capacity_rows, stream=None) -> None:
+    _check_dispatch_buffers(_cfg(cfg), x, recv_x, recv_scales, int(capacity_rows))
     rs = None if recv_scales is None else _ptrs(recv_scales)
     _check(load().ep_dispatch(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)), _ptr(topk_idx),
                               _ptr(x), _ptrs(recv_x), rs, int(capacity_rows), _stream(stream)),
@@ -209,6 +247,7 @@ def ep_dispatch(cfg, handle, topk_idx, x, recv_x, recv_scales, capacity_rows, st
 
 def ep_layout_dispatch(cfg, topk_idx, handle, workspace, x, recv_x, recv_scales, capacity_rows,
                        stream=None) -> None:
+    _check_dispatch_buffers(_cfg(cfg), x, recv_x, recv_scales, int(capacity_rows))
     rs = None if recv_scales is None else _ptrs(recv_scales)
     _check(load().ep_layout_dispatch(ctypes.byref(_cfg(cfg)), _ptr(topk_idx),
                                      ctypes.byref(_handle(handle)), _ptr(workspace), _ptr(x),
@@ -217,6 +256,7 @@ def ep_layout_dispatch(cfg, topk_idx, handle, workspace, x, recv_x, recv_scales,
 
 
 def ep_combine(cfg, handle, topk_idx, recv_y, topk_weights, out, capacity_rows, stream=None) -> None:
+    _check_combine_buffers(_cfg(cfg), recv_y, topk_weights, out, int(capacity_rows))
     _check(load().ep_combine(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)), _ptr(topk_idx),
                              _ptrs(recv_y), _ptr(topk_weights), _ptr(out), int(capacity_rows),
                              _stream(stream)), "ep_combine")
@@ -224,6 +264,9 @@ def ep_combine(cfg, handle, topk_idx, recv_y, topk_weights, out, capacity_rows, 
 
 def ep_combine_shared(cfg, handle, topk_idx, recv_y, topk_weights, shared, out, capacity_rows,
                       stream=None) -> None:
+    c = _cfg(cfg)
+    _check_combine_buffers(c, recv_y, topk_weights, out, int(capacity_rows))
+    _need(shared, c.num_tokens * c.hidden * 2, "shared")
     _check(load().ep_combine_shared(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)),
                                     _ptr(topk_idx), _ptrs(recv_y), _ptr(topk_weights), _ptr(shared),
                                     _ptr(out), int(capacity_rows), _stream(stream)),
@@ -232,6 +275,13 @@ def ep_combine_shared(cfg, handle, topk_idx, recv_y, topk_weights, shared, out, 
 
 def ep_combine_backward(cfg, handle, topk_idx, grad_out, topk_weights, recv_y, grad_recv,
                         grad_weights, capacity_rows, stream=None) -> None:
+    c = _cfg(cfg)
+    cap = int(capacity_rows)
+    _need(grad_out, c.num_tokens * c.hidden * 2, "grad_out")
+    _need(topk_weights, c.num_tokens * c.num_topk * 4, "topk_weights")
+    _need_rows(recv_y, cap, 2 * c.hidden, "recv_y")
+    _need_rows(grad_recv, cap, 2 * c.hidden, "grad_recv")
+    _need(grad_weights, c.num_tokens * c.num_topk * 4, "grad_weights")
     ry = None if recv_y is None else _ptrs(recv_y)
     _check(load().ep_combine_backward(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)),
                                       _ptr(topk_idx), _ptr(grad_out), _ptr(topk_weights), ry,
@@ -242,6 +292,10 @@ def ep_combine_backward(cfg, handle, topk_idx, grad_out, topk_weights, recv_y, g
 
 def ep_silu_mul_quant(cfg, handle, intermediate, act_in, q_out, scales_out, capacity_rows,
                       stream=None) -> None:
+    cap, I = int(capacity_rows), int(intermediate)
+    _need_rows(act_in, cap, 4 * I, "act_in")
+    _need_rows(q_out, cap, I, "q_out")
+    _need_rows(scales_out, cap, 4 * (I // 128), "scales_out")
     _check(load().ep_silu_mul_quant(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)),
                                     int(intermediate), _ptrs(act_in), _ptrs(q_out),
                                     _ptrs(scales_out), int(capacity_rows), _stream(stream)),
@@ -249,6 +303,8 @@ def ep_silu_mul_quant(cfg, handle, intermediate, act_in, q_out, scales_out, capa
 
 
 def ep_unpermute(cfg, handle, topk_idx, recv_y, out, capacity_rows, stream=None) -> None:
+    c = _cfg(cfg)
+    _check_combine_buffers(c, recv_y, None, out, int(capacity_rows), out_rows=c.num_tokens * c.num_topk)
     _check(load().ep_unpermute(ctypes.byref(_cfg(cfg)), ctypes.byref(_handle(handle)), _ptr(topk_idx),
                                _ptrs(recv_y), _ptr(out), int(capacity_rows), _stream(stream)),
            "ep_unpermute")

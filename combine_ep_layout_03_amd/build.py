@@ -34,13 +34,39 @@ def sources() -> list[str]:
     return [os.path.join(CSRC, s) for s in SOURCES]
 
 
+# HIP test kernels under tests/hip/ (each its own small shared library, loaded
+# only by the tests): built with the library's flags and its device headers.
+TEST_HIP = os.path.join(ROOT, "tests", "hip")
+TEST_KERNELS = ["cvt_e4m3"]
+
+
+def test_kernel_path(name: str) -> str:
+    return os.path.join(TEST_HIP, "lib%s.so" % name)
+
+
+def build_test_kernels(verbose: bool = False) -> list[str]:
+    out = []
+    for name in TEST_KERNELS:
+        lib = test_kernel_path(name)
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-shared",
+               os.path.join(TEST_HIP, name + ".hip"), "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
+        out.append(lib)
+    return out
+
+
 EXAMPLE_SRC = os.path.join(ROOT, "examples", "ep_c_example.c")
 EXAMPLE = os.path.join(ROOT, "examples", "ep_c_example")
 
 
 def build(verbose: bool = False) -> str:
     """Compile every source into libep.so (always rebuilds), then the plain-C
-    example program against it.  Returns the library's path."""
+    example program against it and the HIP test kernels.  Returns the
+    library's path."""
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-shared", *sources(), "-o", tmp]
     if verbose:
@@ -48,6 +74,7 @@ def build(verbose: bool = False) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     build_example(verbose)
+    build_test_kernels(verbose)
     return LIB
 
 

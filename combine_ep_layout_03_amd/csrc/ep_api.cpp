@@ -35,8 +35,12 @@ bool handle_ok(const ep_layout_t *h) {
          h->slot_of && h->src_of && h->error_flag;
 }
 
-// The layout reads its chunk table with 16-byte loads.
-bool workspace_ok(const void *ws) { return ws && ((uintptr_t)ws & 15u) == 0; }
+// 16-byte aligned: the row kernels move every row buffer (tokens, received
+// rows, scales, outputs, gradients) with 16-byte vector loads and stores, and
+// the layout reads its chunk table the same way.
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool workspace_ok(const void *ws) { return ws && aligned16(ws); }
 
 ep_status from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
 
@@ -48,24 +52,29 @@ void trace(const char *what, const ep_config *c) {
                c->dispatch_dtype, c->num_workgroups);
 }
 
-// The R receive (and, for FP8, scale) buffers of a dispatch; false if one is NULL.
+// A non-NULL, 16-byte aligned row buffer.
+bool row_buf_ok(const void *p) { return p && aligned16(p); }
+
+// The R receive (and, for FP8, scale) buffers of a dispatch; false if one is
+// NULL or not 16-byte aligned.
 bool recv_ptrs(const ep_config *cfg, void *const *recv_x, float *const *recv_scales,
                ep::RankPtrs &rx, ep::ScalePtrs &rs) {
   const bool fp8 = cfg->dispatch_dtype == EP_DTYPE_FP8_E4M3;
   if (!recv_x || (fp8 && !recv_scales)) return false;
   for (int r = 0; r < cfg->num_ranks; ++r) {
-    if (!recv_x[r] || (fp8 && !recv_scales[r])) return false;
+    if (!row_buf_ok(recv_x[r]) || (fp8 && !row_buf_ok(recv_scales[r]))) return false;
     rx.p[r] = recv_x[r];
     rs.p[r] = fp8 ? recv_scales[r] : nullptr;
   }
   return true;
 }
 
-// R read-only row buffers; false if the array or one pointer is NULL.
+// R read-only row buffers; false if the array or one pointer is NULL or not
+// 16-byte aligned.
 bool const_ptrs(const ep_config *cfg, const void *const *bufs, ep::RankCPtrs &out) {
   if (!bufs) return false;
   for (int r = 0; r < cfg->num_ranks; ++r) {
-    if (!bufs[r]) return false;
+    if (!row_buf_ok(bufs[r])) return false;
     out.p[r] = bufs[r];
   }
   return true;
@@ -153,7 +162,7 @@ ep_status ep_dispatch(const ep_config *cfg, const ep_layout_t *h, const int32_t 
   if (st != EP_OK) return st;
   ep::RankPtrs rx{};
   ep::ScalePtrs rs{};
-  if (!x || !recv_ptrs(cfg, recv_x, recv_scales, rx, rs)) return EP_ERR_INVALID_ARG;
+  if (!row_buf_ok(x) || !recv_ptrs(cfg, recv_x, recv_scales, rx, rs)) return EP_ERR_INVALID_ARG;
   trace("dispatch", cfg);
   return from_hip(ep::launch_dispatch(*cfg, *h, topk_idx, x, rx, rs, capacity_rows, stream));
 }
@@ -168,7 +177,7 @@ ep_status ep_layout_dispatch(const ep_config *cfg, const int32_t *topk_idx, cons
   if (st != EP_OK) return st;
   ep::RankPtrs rx{};
   ep::ScalePtrs rs{};
-  if (!x || !recv_ptrs(cfg, recv_x, recv_scales, rx, rs)) return EP_ERR_INVALID_ARG;
+  if (!row_buf_ok(x) || !recv_ptrs(cfg, recv_x, recv_scales, rx, rs)) return EP_ERR_INVALID_ARG;
   if (ep::fused_layout_dispatch_ok(*cfg)) {
     trace("layout_dispatch (one launch)", cfg);
     return from_hip(
@@ -188,7 +197,7 @@ ep_status ep_combine(const ep_config *cfg, const ep_layout_t *h, const int32_t *
   ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
   if (st != EP_OK) return st;
   ep::RankCPtrs ry{};
-  if (!out || !const_ptrs(cfg, recv_y, ry)) return EP_ERR_INVALID_ARG;
+  if (!row_buf_ok(out) || !const_ptrs(cfg, recv_y, ry)) return EP_ERR_INVALID_ARG;
   trace("combine", cfg);
   return from_hip(ep::launch_combine(*cfg, *h, topk_idx, ry, topk_weights, nullptr, out,
                                      capacity_rows, stream));
@@ -201,7 +210,8 @@ ep_status ep_combine_shared(const ep_config *cfg, const ep_layout_t *h, const in
   ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
   if (st != EP_OK) return st;
   ep::RankCPtrs ry{};
-  if (!out || !shared || !const_ptrs(cfg, recv_y, ry)) return EP_ERR_INVALID_ARG;
+  if (!row_buf_ok(out) || !row_buf_ok(shared) || !const_ptrs(cfg, recv_y, ry))
+    return EP_ERR_INVALID_ARG;
   trace("combine_shared", cfg);
   return from_hip(ep::launch_combine(*cfg, *h, topk_idx, ry, topk_weights, shared, out,
                                      capacity_rows, stream));
@@ -213,13 +223,13 @@ ep_status ep_combine_backward(const ep_config *cfg, const ep_layout_t *h, const 
                               float *grad_weights, int64_t capacity_rows, hipStream_t stream) {
   ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
   if (st != EP_OK) return st;
-  if (!grad_out || !grad_recv) return EP_ERR_INVALID_ARG;
+  if (!row_buf_ok(grad_out) || !grad_recv) return EP_ERR_INVALID_ARG;
   if ((recv_y == nullptr) != (grad_weights == nullptr)) return EP_ERR_INVALID_ARG;
   ep::RankCPtrs ry{};
   ep::RankPtrs rg{};
   if (recv_y && !const_ptrs(cfg, recv_y, ry)) return EP_ERR_INVALID_ARG;
   for (int r = 0; r < cfg->num_ranks; ++r) {
-    if (!grad_recv[r]) return EP_ERR_INVALID_ARG;
+    if (!row_buf_ok(grad_recv[r])) return EP_ERR_INVALID_ARG;
     rg.p[r] = grad_recv[r];
   }
   trace("combine_backward", cfg);
@@ -239,7 +249,8 @@ ep_status ep_silu_mul_quant(const ep_config *cfg, const ep_layout_t *h, int32_t 
   ep::RankPtrs q{};
   ep::ScalePtrs s{};
   for (int r = 0; r < cfg->num_ranks; ++r) {
-    if (!act_in[r] || !q_out[r] || !scales_out[r]) return EP_ERR_INVALID_ARG;
+    if (!row_buf_ok(act_in[r]) || !row_buf_ok(q_out[r]) || !row_buf_ok(scales_out[r]))
+      return EP_ERR_INVALID_ARG;
     in.p[r] = act_in[r];
     q.p[r] = q_out[r];
     s.p[r] = scales_out[r];
@@ -255,7 +266,7 @@ ep_status ep_unpermute(const ep_config *cfg, const ep_layout_t *h, const int32_t
   ep_status st = row_call_ok(cfg, h, topk_idx, capacity_rows);
   if (st != EP_OK) return st;
   ep::RankCPtrs ry{};
-  if (!out || !const_ptrs(cfg, recv_y, ry)) return EP_ERR_INVALID_ARG;
+  if (!row_buf_ok(out) || !const_ptrs(cfg, recv_y, ry)) return EP_ERR_INVALID_ARG;
   trace("unpermute", cfg);
   return from_hip(ep::launch_unpermute(*cfg, *h, topk_idx, ry, out, capacity_rows, stream));
 }

@@ -67,10 +67,10 @@ __device__ inline uint32_t bf16_absbits_max(u32x4 v, uint32_t m) {
 // Four binary32 values (each |v| <= 448 * (1 + 2^-23)) -> four OCP E4M3
 // ("fn": bias 7, max 448, no infinity) codes in one dword, byte i = code of
 // a_i, by gfx950's v_cvt_pk_fp8_f32: nearest with ties to even, saturating at
-// 448, signed zeros kept.  On MI355X it was compared, over every binary32
-// pattern with |v| <= 450 (both signs), with an encoder that rounds the
-// binary32 significand to 3 bits on the bit pattern (rint(|v| * 2^9) below
-// 2^-6): no mismatch.  A block quotient x/s never exceeds 448 * (1 + 2^-23).
+// 448, signed zeros kept.  tests/test_gpu_cvt.py compares it code for code
+// with the oracle's encoder on every binary32 value within 2^12 ulps of each
+// E4M3 value and rounding midpoint and on every 257th pattern up to |v| = 450,
+// both signs.  A block quotient x/s never exceeds 448 * (1 + 2^-23).
 __device__ inline uint32_t e4m3_pack4(float a0, float a1, float a2, float a3) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, w, true);

@@ -157,8 +157,9 @@ __global__ __launch_bounds__(kWave) void layout_dispatch_small_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) c[q] = wave_sum_u32(c[q]);
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        if (lane == j0 + jj) my_slot = off[ej[jj]] + (int32_t)((c[jj / 2] >> (16 * (jj & 1))) & 0xFFFFu);
+      for (int jj = 0; jj < 8; ++jj)  // pairs j0 + jj >= k have no expert (ej = -1)
+        if (j0 + jj < k && lane == j0 + jj)
+          my_slot = off[ej[jj]] + (int32_t)((c[jj / 2] >> (16 * (jj & 1))) & 0xFFFFu);
     }
     for (int j = 0; j < k; ++j) my_slot += (j < lane && (int32_t)rdl((uint32_t)my_e, j) == my_e) ? 1 : 0;
     uint64_t dst = 0, sdst = 0;

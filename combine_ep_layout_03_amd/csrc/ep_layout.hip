@@ -113,12 +113,16 @@ using dev::wave_inclusive_scan;
 // Chunk histograms: wave c counts the pairs [c*S, c*S+S) in LDS and writes
 // them to the table hist[C/4][E+1][4]: workgroup g's kLayoutWaves chunks form
 // one 16-byte group per expert (entry E counts indices outside [0,E)).
+// The first of two launches, so it also clears the handle's error word: the
+// scatter kernel after it only ORs bits in.
 __global__ __launch_bounds__(kThreads) void layout_count_kernel(const int32_t *__restrict__ idx,
                                                                  int64_t P, int32_t E, int32_t S,
                                                                  int32_t C,
-                                                                 int32_t *__restrict__ hist) {
+                                                                 int32_t *__restrict__ hist,
+                                                                 int32_t *__restrict__ err) {
   extern __shared__ int32_t lds[];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
   const int E1 = E + 1;
   int32_t *h = lds + wave * E1;
   for (int e = lane; e < E1; e += kWave) h[e] = 0;
@@ -183,8 +187,11 @@ __device__ void block_exclusive_scan(int32_t *a, int n, int32_t *wsum) {
 }
 
 // Counts, offsets, rank ranges and error word from the scanned offsets
-// off[0..E] (every thread of the workgroup takes part).
-template <int NT>
+// off[0..E] (every thread of the workgroup takes part).  RESET: a one-launch
+// layout stores the word (0 or EP_DEVERR_INDEX) from its workgroup 0, the one
+// workgroup that ever writes it in that launch; the second launch of a
+// two-launch layout, whose first launch cleared it, only ORs the bit in.
+template <int NT, bool RESET>
 __device__ void write_handle(const int32_t *off, int32_t E, int32_t R, int32_t nbad,
                              const ep_layout_t &h) {
   const int tid = threadIdx.x;
@@ -200,7 +207,12 @@ __device__ void write_handle(const int32_t *off, int32_t E, int32_t R, int32_t n
   if (tid == 0) {
     h.expert_offsets[E] = off[E];
     h.rank_offsets[R] = off[E];
-    h.error_flag[0] = nbad ? (int32_t)EP_DEVERR_INDEX : 0;
+    if (RESET) {
+      h.error_flag[0] = nbad ? (int32_t)EP_DEVERR_INDEX : 0;
+      __threadfence();  // ordered before this workgroup's own walk
+    } else if (nbad) {
+      atomicOr(h.error_flag, (int32_t)EP_DEVERR_INDEX);
+    }
   }
 }
 
@@ -235,10 +247,15 @@ __device__ inline void load_stage(const int32_t *__restrict__ idx, int64_t qb, i
 }
 
 // `first`, if given, holds this lane's load_stage of the first stage (p0),
-// issued earlier by the caller so that its latency overlaps other work.
+// issued earlier by the caller so that its latency overlaps other work.  A
+// slot outside [0,P) cannot happen; should it, the pair's slot_of is -1, so
+// every later call on the handle reports EP_DEVERR_ROW for its token, and
+// EP_DEVERR_INTERNAL is ORed into the error word where that cannot race with
+// the word's reset (`flag`: the second launch of a two-launch layout, or
+// workgroup 0 of a one-launch layout after its own store).
 template <int PL>
 __device__ void wave_walk(const int32_t *__restrict__ idx, int64_t p0, int64_t p1, int64_t P,
-                          int32_t E, int32_t *bw, int32_t *stage, const ep_layout_t &h,
+                          int32_t E, int32_t *bw, int32_t *stage, const ep_layout_t &h, bool flag,
                           const i32x4 *first = nullptr) {
   static_assert(PL % 4 == 0, "whole 16-byte groups per lane");
   constexpr int kSt = PL * kWave;
@@ -287,9 +304,13 @@ __device__ void wave_walk(const int32_t *__restrict__ idx, int64_t p0, int64_t p
         if (valid[s]) {
           const int64_t p = qb + (int64_t)(i0 + s) * kWave + lane;
           const int32_t slot = bw[e[s]] + __popcll(m[s] & below);
-          h.slot_of[p] = slot;
-          if ((uint64_t)(uint32_t)slot < (uint64_t)P) h.src_of[slot] = (int32_t)p;
-          else atomicOr(h.error_flag, (int32_t)EP_DEVERR_INTERNAL);  // cannot happen; never write out of range
+          if ((uint64_t)(uint32_t)slot < (uint64_t)P) {
+            h.slot_of[p] = slot;
+            h.src_of[slot] = (int32_t)p;
+          } else {  // cannot happen; never write out of range
+            h.slot_of[p] = -1;
+            if (flag) atomicOr(h.error_flag, (int32_t)EP_DEVERR_INTERNAL);
+          }
           if ((m[s] >> lane) == 1ull) bw[e[s]] += __popcll(m[s]);  // the group's highest lane
         }
       }
@@ -363,10 +384,12 @@ __global__ __launch_bounds__(kWave) void layout_tiny_kernel(const int32_t *__res
       h.rank_offsets[r] = tot[r * El];
       h.rank_counts[r] = tot[(r + 1) * El] - tot[r * El];
     }
-    if (lane == 0) {
+    if (lane == 0) {  // the only writer of the error word in this launch but for
+                      // workgroup 0's own internal check below
       h.expert_offsets[E] = tot[E];
       h.rank_offsets[R] = tot[E];
       h.error_flag[0] = bad ? (int32_t)EP_DEVERR_INDEX : 0;
+      __threadfence();
     }
   }
   if (bad) return;  // uniform: the handle's slots are unspecified on error
@@ -382,9 +405,13 @@ __global__ __launch_bounds__(kWave) void layout_tiny_kernel(const int32_t *__res
   if (own) {
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
     const int32_t slot = tot[pe] + pre[pe] + __popcll(m & below);
-    h.slot_of[p] = slot;
-    if ((uint64_t)(uint32_t)slot < (uint64_t)P) h.src_of[slot] = (int32_t)p;
-    else atomicOr(h.error_flag, (int32_t)EP_DEVERR_INTERNAL);  // cannot happen; never write out of range
+    if ((uint64_t)(uint32_t)slot < (uint64_t)P) {
+      h.slot_of[p] = slot;
+      h.src_of[slot] = (int32_t)p;
+    } else {  // cannot happen; never write out of range (see wave_walk)
+      h.slot_of[p] = -1;
+      if (blockIdx.x == 0) atomicOr(h.error_flag, (int32_t)EP_DEVERR_INTERNAL);
+    }
   }
 }
 
@@ -464,13 +491,14 @@ __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
   int32_t nbad = 0;
   for (int w = 0; w < kSmallWaves; ++w) nbad += misc[kSmallWaves + w];
   block_exclusive_scan<kSmallThreads>(tot, E, misc);  // synchronizes
-  if (blockIdx.x == 0) write_handle<kSmallThreads>(tot, E, R, nbad, h);
+  if (blockIdx.x == 0) write_handle<kSmallThreads, true>(tot, E, R, nbad, h);
   if (nbad) return;  // uniform: the handle's slots are unspecified on error
   for (int i = tid; i < kSmallWaves * E; i += kSmallThreads) cnt[i] += tot[i % E];
   __syncthreads();
   const int64_t p0 = c0 + (int64_t)wave * Sw;
   const int64_t p1 = (p0 + Sw < c1) ? p0 + Sw : c1;
-  wave_walk<kSmallStage / kWave>(idx, p0, p1, P, E, cnt + wave * E, stage + wave * kSmallStage, h);
+  wave_walk<kSmallStage / kWave>(idx, p0, p1, P, E, cnt + wave * E, stage + wave * kSmallStage, h,
+                                 blockIdx.x == 0);
 }
 
 __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
@@ -541,14 +569,15 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
 #pragma unroll
   for (int w = 0; w < kLayoutWaves; ++w) nbad += misc[kLayoutWaves + w];
   block_exclusive_scan<kThreads>(off, E, misc);
-  if (blockIdx.x == 0) write_handle<kThreads>(off, E, R, nbad, h);
+  if (blockIdx.x == 0) write_handle<kThreads, false>(off, E, R, nbad, h);
   if (nbad) return;  // uniform: the handle's slots are unspecified on error
 
   for (int i = tid; i < kLayoutWaves * E; i += kThreads) base[i] += off[i % E];
   __syncthreads();
 
   if (wc >= C) return;
-  wave_walk<kStage / kWave>(idx, wp0, wp1, P, E, base + wave * E, stage + wave * kStage, h, first);
+  wave_walk<kStage / kWave>(idx, wp0, wp1, P, E, base + wave * E, stage + wave * kStage, h, true,
+                            first);
 }
 
 }  // namespace
@@ -572,7 +601,7 @@ hipError_t launch_layout(const ep_config &c, const LayoutPlan &plan, const int32
   int32_t *hist = static_cast<int32_t *>(workspace);
   const size_t lds_count = (size_t)kLayoutWaves * (E + 1) * sizeof(int32_t);
   hipLaunchKernelGGL(layout_count_kernel, dim3(plan.workgroups), dim3(kThreads), lds_count, s,
-                     topk_idx, plan.P, E, plan.S, plan.C, hist);
+                     topk_idx, plan.P, E, plan.S, plan.C, hist, h.error_flag);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_layout_scatter(c, plan, topk_idx, h, workspace, s);

@@ -14,8 +14,10 @@
 // Lane l holds the NPER consecutive experts [l*NPER, (l+1)*NPER) in
 // registers (NPER a power of two, 64*NPER >= El).  The gate is evaluated in
 // binary64 and rounded once to binary32, so the scores -- and with them every
-// selection, which compares binary32 values only -- do not depend on how a
-// device or host libm rounds its exp.  Scores are non-negative, so their bit
+// selection, which compares binary32 values only -- barely depend on how a
+// device or host libm rounds its exp; the softmax denominator is the binary64
+// sum of the numerators in ascending expert order (a serial fold over the
+// lanes), the order a plain loop over the experts takes.  Scores are non-negative, so their bit
 // patterns order like the values; a wave maximum of 32-bit patterns is four
 // DPP steps inside each row of 16 lanes, four readlanes and a scalar max, and
 // a ballot of the lanes holding that maximum names the winner: the lowest such
@@ -65,26 +67,18 @@ __device__ inline float wave_max_f32(float v) {
   return fmaxf(a, b);
 }
 
-template <int CTRL>
-__device__ inline double dpp_f64(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint64_t lo = dpp<CTRL>((uint32_t)u), hi = dpp<CTRL>((uint32_t)(u >> 32));
-  return __longlong_as_double((long long)((hi << 32) | lo));
-}
-
 __device__ inline double rdl_f64(double v, int lane) {
   const uint64_t u = (uint64_t)__double_as_longlong(v);
   return __longlong_as_double(
       (long long)(((uint64_t)rdl((uint32_t)(u >> 32), lane) << 32) | rdl((uint32_t)u, lane)));
 }
 
-// Sum over the wave in binary64 (a fixed tree), uniform result.
-__device__ inline double wave_sum_f64(double v) {
-  v += dpp_f64<kDppXor1>(v);
-  v += dpp_f64<kDppXor2>(v);
-  v += dpp_f64<kDppHalfMirror>(v);
-  v += dpp_f64<kDppMirror>(v);
-  return (rdl_f64(v, 0) + rdl_f64(v, 16)) + (rdl_f64(v, 32) + rdl_f64(v, 48));
+// Value of `src`'s v in every lane (src may differ between lanes).
+__device__ inline double shfl_f64(double v, int src) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)u, src, kWave);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(u >> 32), src, kWave);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 // Value of lane (lane ^ off) for off a power of two below 64.
@@ -156,13 +150,16 @@ __global__ __launch_bounds__(kWave) void route_kernel(
         if ((valid >> i) & 1u) m = fmaxf(m, z[i]);
       m = wave_max_f32(m);
       double ex[NPER];
-      double sum = 0.0;
 #pragma unroll
-      for (int i = 0; i < NPER; ++i) {
-        ex[i] = ((valid >> i) & 1u) ? exp((double)z[i] - (double)m) : 0.0;
-        sum += ex[i];
+      for (int i = 0; i < NPER; ++i) ex[i] = ((valid >> i) & 1u) ? exp((double)z[i] - (double)m) : 0.0;
+      // the denominator in ascending expert order, one binary64 addition at a
+      // time (lane l holds experts l*NPER ..); the padding past El adds +0
+      double sum = 0.0;
+      const int nl = (El + NPER - 1) / NPER;
+      for (int l = 0; l < nl; ++l) {
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) sum += rdl_f64(ex[i], l);
       }
-      sum = wave_sum_f64(sum);
 #pragma unroll
       for (int i = 0; i < NPER; ++i) s[i] = (float)(ex[i] / sum);
     } else {
@@ -290,7 +287,7 @@ __global__ __launch_bounds__(kWave) void route_kernel(
 // ---- four tokens per wave ------------------------------------------------
 // For T >= kRowMinTokens, El <= 512, k <= 16 and groups covering power-of-two
 // runs of at most 16 lanes, each 16-lane row of the wave routes its own token: the same four DPP
-// steps then leave every lane of a row holding that row's maximum or sum (no
+// steps then leave every lane of a row holding that row's maximum (no
 // readlanes), one ballot serves the four tokens' picks, and the winner's
 // local index comes over with one shuffle, so the serial pick chain is shared
 // by four tokens.  Results are those of route_kernel bit for bit (same
@@ -316,13 +313,6 @@ __device__ inline float row_max_f32(float v) {
   v = fmaxf(v, __uint_as_float(dpp<kDppXor2>(__float_as_uint(v))));
   v = fmaxf(v, __uint_as_float(dpp<kDppHalfMirror>(__float_as_uint(v))));
   return fmaxf(v, __uint_as_float(dpp<kDppMirror>(__float_as_uint(v))));
-}
-
-__device__ inline double row_sum_f64(double v) {
-  v += dpp_f64<kDppXor1>(v);
-  v += dpp_f64<kDppXor2>(v);
-  v += dpp_f64<kDppHalfMirror>(v);
-  return v + dpp_f64<kDppMirror>(v);
 }
 
 // Winner of each row among its offering lanes: the largest bits, then the
@@ -352,7 +342,7 @@ __global__ __launch_bounds__(COUNT ? kWave * kRouteCountWaves : kWave) void rout
     const int32_t *__restrict__ rep_off, const int32_t *__restrict__ rep_slots, int32_t T,
     int32_t El, int32_t k, int32_t gate, int32_t G, int32_t TG, int32_t topn, int32_t renorm,
     int32_t *__restrict__ idx, float *__restrict__ wout, int32_t E, int32_t tpc, int32_t C,
-    int32_t *__restrict__ hist) {
+    int32_t *__restrict__ hist, int32_t *__restrict__ err) {
   extern __shared__ int32_t cnt[];  // COUNT: [E+1] this chunk's expert histogram
   const int lane = threadIdx.x % kWave, row = lane / kRowLanes, lr = lane % kRowLanes;
   const int e0 = lr * NPER;
@@ -366,6 +356,7 @@ __global__ __launch_bounds__(COUNT ? kWave * kRouteCountWaves : kWave) void rout
 
   int64_t tb0 = (int64_t)blockIdx.x * kRowTokens, tend = T, tstep = (int64_t)gridDim.x * kRowTokens;
   if (COUNT) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
     for (int e = threadIdx.x; e <= E; e += kWave * kRouteCountWaves) cnt[e] = 0;
     __syncthreads();
     const int64_t c0 = (int64_t)blockIdx.x * tpc;
@@ -408,13 +399,17 @@ __global__ __launch_bounds__(COUNT ? kWave * kRouteCountWaves : kWave) void rout
         if ((valid >> i) & 1u) m = fmaxf(m, z[i]);
       m = row_max_f32(m);
       double ex[NPER];
-      double sum = 0.0;
 #pragma unroll
-      for (int i = 0; i < NPER; ++i) {
-        ex[i] = ((valid >> i) & 1u) ? exp((double)z[i] - (double)m) : 0.0;
-        sum += ex[i];
+      for (int i = 0; i < NPER; ++i) ex[i] = ((valid >> i) & 1u) ? exp((double)z[i] - (double)m) : 0.0;
+      // the denominator in ascending expert order, as in route_kernel: lane
+      // l of the row holds experts l*NPER ..; every lane of the row folds the
+      // row's values in that order
+      double sum = 0.0;
+      const int nl = (El + NPER - 1) / NPER;
+      for (int l = 0; l < nl; ++l) {
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) sum += shfl_f64(ex[i], row * kRowLanes + l);
       }
-      sum = row_sum_f64(sum);
 #pragma unroll
       for (int i = 0; i < NPER; ++i) s[i] = (float)(ex[i] / sum);
     } else {
@@ -547,7 +542,7 @@ template <bool COUNT>
 hipError_t launch_rows(const ep_config &c, const ep_router_t &rt, int nrow, const float *logits,
                        const float *bias, const int32_t *rep_off, const int32_t *rep_slots,
                        int32_t *topk_idx, float *topk_w, const LayoutPlan &plan, int32_t *hist,
-                       hipStream_t s) {
+                       int32_t *err, hipStream_t s) {
   const int grid = COUNT ? plan.C : row_grid(c, (c.num_tokens + kRowTokens - 1) / kRowTokens);
   const int block = COUNT ? kWave * kRouteCountWaves : kWave;
   const size_t lds = COUNT ? (size_t)(c.num_experts + 1) * sizeof(int32_t) : 0;
@@ -555,7 +550,7 @@ hipError_t launch_rows(const ep_config &c, const ep_router_t &rt, int nrow, cons
   hipLaunchKernelGGL((route_rows_kernel<N, COUNT>), dim3(grid), dim3(block), lds, s, logits,     \
                      bias, rep_off, rep_slots, c.num_tokens, rt.num_logical, c.num_topk, rt.gate, \
                      rt.num_groups, rt.topk_groups, rt.group_topn, rt.renormalize, topk_idx,    \
-                     topk_w, c.num_experts, plan.tpc, plan.C, hist)
+                     topk_w, c.num_experts, plan.tpc, plan.C, hist, err)
   switch (nrow) {
     case 1: EP_ROUTE_ROWS(1); break;
     case 2: EP_ROUTE_ROWS(2); break;
@@ -578,7 +573,7 @@ hipError_t launch_route(const ep_config &c, const ep_router_t &rt, const float *
   const int nrow = rows_nper(c, rt);
   if (nrow > 0)
     return launch_rows<false>(c, rt, nrow, logits, bias, rep_off, rep_slots, topk_idx, topk_w,
-                              LayoutPlan{}, nullptr, s);
+                              LayoutPlan{}, nullptr, nullptr, s);
   const int grid = row_grid(c, c.num_tokens);
   const size_t lds = (size_t)rt.num_logical * sizeof(float);  // scores, for the LDS group path
 #define EP_ROUTE_LAUNCH(N)                                                                     \
@@ -609,7 +604,8 @@ hipError_t launch_route_layout(const ep_config &c, const ep_router_t &rt, const 
                          topk_idx, h, workspace, s);
   }
   const hipError_t err = launch_rows<true>(c, rt, nrow, logits, bias, rep_off, rep_slots, topk_idx,
-                                           topk_w, fp, static_cast<int32_t *>(workspace), s);
+                                           topk_w, fp, static_cast<int32_t *>(workspace),
+                                           h.error_flag, s);
   if (err != hipSuccess) return err;
   return launch_layout_scatter(c, fp, topk_idx, h, workspace, s);
 }

@@ -45,7 +45,16 @@
  *     can be captured into a hipGraph (no host sync, no allocation, no memset
  *     nodes).
  *   - Host-checkable problems (NULL pointers, bad sizes, too small a
- *     capacity) return a nonzero ep_status at once and enqueue nothing.
+ *     capacity, a misaligned row buffer) return a nonzero ep_status at once
+ *     and enqueue nothing.
+ *   - Row buffers must be 16-byte aligned (EP_ERR_INVALID_ARG otherwise):
+ *     x, recv_x[r], recv_scales[r], recv_y[r], out, shared, grad_out,
+ *     grad_recv[r], act_in[r], q_out[r], scales_out[r] and the layout
+ *     workspace.  The kernels move rows with 16-byte vector loads and stores;
+ *     every row pitch is a multiple of 16 bytes by the size rules above, so
+ *     an aligned base aligns every row.  Any device allocation is aligned;
+ *     a view that starts inside a row is not.  The index, weight and logit
+ *     arrays need only their element alignment.
  *   - Data problems found on the device (a routing index outside [0,E), a
  *     row outside the capacity) set bits in the handle's error word; every
  *     call that reads a handle (dispatch, combine with or without the shared
@@ -85,10 +94,19 @@ typedef int32_t ep_status;
 #define EP_ERR_CAPACITY 3    /* capacity_rows below ep_recv_capacity_rows() */
 #define EP_ERR_HIP 4         /* a HIP launch failed (hipGetLastError) */
 
-/* Bits of the device error word (ep_layout_t.error_flag[0]). */
+/* Bits of the device error word (ep_layout_t.error_flag[0]).  The layout
+ * (ep_layout, ep_layout_dispatch, ep_route_layout) rewrites the word: it
+ * clears it and sets EP_DEVERR_INDEX, in an order no other write of the same
+ * layout can overtake (a two-launch layout clears it in its first launch; a
+ * one-launch layout has one workgroup write it).  Later calls only OR bits
+ * in. */
 #define EP_DEVERR_INDEX 1u    /* ep_layout saw an index outside [0,E) */
 #define EP_DEVERR_ROW 2u      /* dispatch/combine saw a row outside [0,capacity) */
-#define EP_DEVERR_INTERNAL 4u /* ep_layout computed a slot outside [0,T*k): a library bug */
+#define EP_DEVERR_INTERNAL 4u /* ep_layout computed a slot outside [0,T*k): a library
+                                 bug.  Such a pair's slot_of is -1, so later calls on
+                                 the handle report EP_DEVERR_ROW for its token even
+                                 where the layout could not set this bit without a
+                                 race (a one-launch layout's other workgroups). */
 
 typedef int32_t ep_dtype;
 #define EP_DTYPE_BF16 0     /* dispatch copies bf16 rows */
@@ -262,8 +280,9 @@ ep_status ep_combine_backward(const ep_config *cfg /*(host)*/, const ep_layout_t
  * split from device-side token counts under graphs).  For every received row
  * (the T*k slots, mapped to rank r and row with the handle's rank_offsets on
  * the device): gate = act_in row [0, I), up = [I, 2I) (bf16);
- *   a = g * rcp(1 + expf(-g)) * u in fp32 (the device library's expf and
- *   the hardware reciprocal; a few fp32 ulps from the binary64 value), then
+ *   a = g * rcp(1 + e^-g) * u in fp32, with e^-g from the hardware base-2
+ *   exponential after a split-constant argument reduction and the hardware
+ *   reciprocal (within 2.34 fp32 ulps of the binary64 value), then
  *   per 128-element block s = a_max/448 (correctly rounded) and
  *   q = E4M3(a * (1/s)) (one divide per block; exact a/s for blocks whose
  *   1/s overflows).
@@ -285,7 +304,8 @@ ep_status ep_silu_mul_quant(const ep_config *cfg /*(host)*/, const ep_layout_t *
  * node-limited routing).  For each token t, with logits [T, El] fp32:
  *   z[e] = logits[t][e] + bias[e]  (one fp32 add; bias [El] may be NULL);
  *   s[e] = gate score evaluated in binary64 and rounded once to fp32:
- *          softmax exp(z_e - max z) / sum exp(z_i - max z), or sigmoid
+ *          softmax exp(z_e - max z) / sum exp(z_i - max z), the sum taken
+ *          in ascending i (one binary64 addition at a time), or sigmoid
  *          1 / (1 + exp(-z_e));
  *   each group of El/G consecutive experts scores its best s (group_topn 1)
  *          or the fp32 sum of its two best; the TG best groups stay eligible;

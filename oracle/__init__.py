@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_quantize_f32_row.argtypes = [i32, vp, vp, vp]
         L.oracle_route.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.oracle_route.restype = i32
+        L.oracle_route_scores.argtypes = [i32, i32, i32, vp, vp, vp]
+        L.oracle_route_scores.restype = i32
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
@@ -335,6 +337,20 @@ def dequant_identity_expert(recv_q, recv_s):
 
 # ----------------------------------------------------------------- router
 GATES = {"softmax": 0, "sigmoid": 1}
+
+
+def route_scores(logits: np.ndarray, gate: str = "sigmoid", bias=None) -> np.ndarray:
+    """The router's gate scores (oracle_route_scores): [T, El] float32, the
+    binary64 gate of logit + bias rounded once to binary32."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, El = logits.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty((T, El), np.float32)
+    rc = lib().oracle_route_scores(T, El, GATES[gate], _p(logits), None if b is None else _p(b),
+                                   _p(out))
+    if rc:
+        raise OracleError("router parameters rejected (code %d)" % rc)
+    return out
 
 
 def route(logits: np.ndarray, k: int, gate: str = "sigmoid", n_groups: int = 1,

@@ -433,6 +433,48 @@ static int ranks_above(float sa, int a, float sb, int b)
     return a < b;
 }
 
+/* One token's gate scores s[0..El) from its logits row: the router input is
+ * the logit plus the per-expert bias (one binary32 add); the gate is
+ * evaluated in binary64 and rounded once to binary32.  Softmax subtracts the
+ * maximum input and divides by the binary64 sum of the numerators taken in
+ * ascending expert order.  z and ex are scratch rows of El entries. */
+static void gate_scores(int El, int gate, const float *lrow, const float *bias, float *z, double *ex,
+                        float *s)
+{
+    for (int e = 0; e < El; ++e)
+        z[e] = bias ? lrow[e] + bias[e] : lrow[e];
+    if (gate == 0) { /* softmax over the token's experts, max-subtracted */
+        float m = z[0];
+        for (int e = 1; e < El; ++e)
+            if (z[e] > m)
+                m = z[e];
+        double sum = 0.0;
+        for (int e = 0; e < El; ++e) {
+            ex[e] = exp((double)z[e] - (double)m);
+            sum += ex[e];
+        }
+        for (int e = 0; e < El; ++e)
+            s[e] = (float)(ex[e] / sum);
+    } else { /* sigmoid */
+        for (int e = 0; e < El; ++e)
+            s[e] = (float)(1.0 / (1.0 + exp(-(double)z[e])));
+    }
+}
+
+int oracle_route_scores(int T, int El, int gate, const float *logits, const float *bias,
+                        float *scores)
+{
+    if (T < 1 || El < 1 || (gate != 0 && gate != 1))
+        return 1;
+    float *z = malloc(sizeof(float) * (size_t)El);
+    double *ex = malloc(sizeof(double) * (size_t)El);
+    for (int t = 0; t < T; ++t)
+        gate_scores(El, gate, logits + (int64_t)t * El, bias, z, ex, scores + (int64_t)t * El);
+    free(z);
+    free(ex);
+    return 0;
+}
+
 int oracle_route(int T, int El, int k, int gate, int G, int TG, int group_topn, int renorm,
                  const float *logits, const float *bias, const int32_t *rep_off,
                  const int32_t *rep_slots, int32_t *idx, float *w)
@@ -455,27 +497,7 @@ int oracle_route(int T, int El, int k, int gate, int G, int TG, int group_topn, 
     float *ws = malloc(sizeof(float) * (size_t)k);
 
     for (int t = 0; t < T; ++t) {
-        /* router input: logit plus the per-expert bias (one binary32 add) */
-        for (int e = 0; e < El; ++e)
-            z[e] = bias ? logits[(int64_t)t * El + e] + bias[e] : logits[(int64_t)t * El + e];
-
-        /* gate scores, evaluated in binary64 and rounded once to binary32 */
-        if (gate == 0) { /* softmax over the token's experts, max-subtracted */
-            float m = z[0];
-            for (int e = 1; e < El; ++e)
-                if (z[e] > m)
-                    m = z[e];
-            double sum = 0.0;
-            for (int e = 0; e < El; ++e) {
-                ex[e] = exp((double)z[e] - (double)m);
-                sum += ex[e];
-            }
-            for (int e = 0; e < El; ++e)
-                s[e] = (float)(ex[e] / sum);
-        } else { /* sigmoid */
-            for (int e = 0; e < El; ++e)
-                s[e] = (float)(1.0 / (1.0 + exp(-(double)z[e])));
-        }
+        gate_scores(El, gate, logits + (int64_t)t * El, bias, z, ex, s);
 
         /* group-limited routing: a group's score is its best score, or the
          * binary32 sum of its two best; the TG best groups stay eligible.

@@ -133,6 +133,11 @@ void oracle_quantize_f32_row(int n, const float *a, uint8_t *q, float *s);
  *          rep_off[l] (-1 when n_l = 0), or l itself when rep_off is NULL.
  * Returns 1 (outputs untouched) unless 1 <= k <= El, G | El, 1 <= TG <= G,
  * k <= TG*El/G, gate in {0,1}, group_topn in {1,2}. */
+/* The router's gate scores alone: scores [T, El] binary32, each the binary64
+ * gate rounded once (the first step of oracle_route).  Returns nonzero for
+ * T < 1, El < 1 or an unknown gate. */
+int oracle_route_scores(int T, int El, int gate, const float *logits, const float *bias,
+                        float *scores);
 int oracle_route(int T, int El, int k, int gate, int G, int TG, int group_topn, int renorm,
                  const float *logits, const float *bias, const int32_t *rep_off,
                  const int32_t *rep_slots, int32_t *idx, float *w);

@@ -210,3 +210,70 @@ def test_header_is_plain_c():
                         os.path.join(root, "examples", "ep_c_example.c")],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
+
+
+A, M = 4096, 4104   # fake device addresses: 16-byte aligned, and 8- but not 16-byte aligned
+
+
+def _misaligned_cases():
+    c = ep.Config(16, 256, 2, 16, 4)
+    cf = ep.Config(16, 256, 2, 16, 4, fp8=True)
+    h = _lib.ep_layout_t(*([A] * 7))
+    R, cap = 4, 32
+
+    def rows(bad=None):
+        return [M if r == bad else A for r in range(R)]
+
+    return {
+        "dispatch x": lambda: ep.ep_dispatch(c, h, A, M, rows(), None, cap, 0),
+        "dispatch recv_x": lambda: ep.ep_dispatch(c, h, A, A, rows(2), None, cap, 0),
+        "dispatch recv_scales": lambda: ep.ep_dispatch(cf, h, A, A, rows(), rows(1), cap, 0),
+        "layout_dispatch x": lambda: ep.ep_layout_dispatch(cf, A, h, A, M, rows(), rows(), cap, 0),
+        "layout_dispatch recv_x": lambda: ep.ep_layout_dispatch(cf, A, h, A, A, rows(0), rows(), cap, 0),
+        "combine out": lambda: ep.ep_combine(c, h, A, rows(), A, M, cap, 0),
+        "combine recv_y": lambda: ep.ep_combine(c, h, A, rows(3), A, A, cap, 0),
+        "combine_shared shared": lambda: ep.ep_combine_shared(c, h, A, rows(), A, M, A, cap, 0),
+        "combine_shared out": lambda: ep.ep_combine_shared(c, h, A, rows(), A, A, M, cap, 0),
+        "combine_backward grad_out": lambda: ep.ep_combine_backward(c, h, A, M, A, rows(), rows(), A,
+                                                                   cap, 0),
+        "combine_backward grad_recv": lambda: ep.ep_combine_backward(c, h, A, A, A, rows(), rows(0), A,
+                                                                    cap, 0),
+        "combine_backward recv_y": lambda: ep.ep_combine_backward(c, h, A, A, A, rows(1), rows(), A,
+                                                                 cap, 0),
+        "silu act_in": lambda: ep.ep_silu_mul_quant(c, h, 128, rows(2), rows(), rows(), cap, 0),
+        "silu q_out": lambda: ep.ep_silu_mul_quant(c, h, 128, rows(), rows(0), rows(), cap, 0),
+        "silu scales_out": lambda: ep.ep_silu_mul_quant(c, h, 128, rows(), rows(), rows(3), cap, 0),
+        "unpermute out": lambda: ep.ep_unpermute(c, h, A, rows(), M, cap, 0),
+        "unpermute recv_y": lambda: ep.ep_unpermute(c, h, A, rows(0), A, cap, 0),
+    }
+
+
+@pytest.mark.parametrize("case", sorted(_misaligned_cases()))
+def test_row_buffers_must_be_16_byte_aligned(lib, case):
+    """Every row buffer is moved with 16-byte vector loads and stores, so a
+    pointer that is not 16-byte aligned is rejected on the host (nothing is
+    launched: exactly one argument of each call is bad)."""
+    with pytest.raises(ep.EpError) as ei:
+        _misaligned_cases()[case]()
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+
+
+def test_binding_checks_tensor_sizes():
+    """The binding rejects a tensor smaller than the rows the call addresses
+    (CPU tensors suffice: the check runs before any pointer is taken)."""
+    import torch
+    c = ep.Config(16, 256, 2, 16, 4, fp8=True)
+    h = _lib.ep_layout_t(*([A] * 7))
+    small = torch.empty(10, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="x holds"):
+        ep.ep_dispatch(c, h, A, small, [A] * 4, [A] * 4, 32, 0)
+    with pytest.raises(ValueError, match=r"recv_x\[1\]"):
+        ep.ep_dispatch(c, h, A, A, [A, small, A, A], [A] * 4, 32, 0)
+    with pytest.raises(ValueError, match=r"recv_scales\[0\]"):
+        ep.ep_dispatch(c, h, A, A, [A] * 4, [small, A, A, A], 32, 0)
+    with pytest.raises(ValueError, match="out holds"):
+        ep.ep_combine(c, h, A, [A] * 4, None, small, 32, 0)
+    with pytest.raises(ValueError, match=r"grad_recv\[3\]"):
+        ep.ep_combine_backward(c, h, A, A, None, None, [A, A, A, small], None, 32, 0)
+    with pytest.raises(ValueError, match=r"q_out\[2\]"):
+        ep.ep_silu_mul_quant(c, h, 128, [A] * 4, [A, A, small, A], [A] * 4, 32, 0)

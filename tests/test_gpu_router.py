@@ -1,12 +1,14 @@
 """GPU parity of ep_route / ep_route_layout (the on-device router feeding the
 layout) against the oracle's router, through the C ABI.
 
-Both sides round the binary64 gate once to binary32 and take every decision
-(groups, top-k, ties) on those binary32 values, so indices and weights are
-compared bit for bit.  (A device exp and a host exp may differ in the last
-binary64 bit; that changes a binary32 score only when the binary64 value
-sits within that bit of a binary32 rounding boundary, which none of these
-seeded cases hits.)
+Both sides round the binary64 gate once to binary32, sum the softmax
+denominator in ascending expert order and take every decision (groups, top-k,
+ties) on those binary32 values, so indices and weights are expected to match
+bit for bit.  A device exp and a host exp may still differ in the last
+binary64 bit, which moves a binary32 score by at most one ulp; a token whose
+result is not bit-identical is therefore checked with the validity rule of
+tests/router_validity.py (the exact result for scores within one ulp of the
+oracle's), and the number of such tokens is printed.
 """
 import numpy as np
 import pytest
@@ -17,6 +19,7 @@ import oracle
 from workloads import CONFIGS, make_workload
 
 from gpu_util import POISON, GpuRun, say, to_dev
+from router_validity import invalid_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -43,14 +46,25 @@ def run_route(T, k, E, logits, gate="sigmoid", n_groups=1, topk_groups=1, group_
     return idx.cpu().numpy(), w.cpu().numpy()
 
 
+def check_routing(gi, gw, logits, k, **kw):
+    """The device's routing against the oracle's: bit-identical tokens pass,
+    any other token must satisfy the validity rule."""
+    okw = {a: b for a, b in kw.items() if a != "num_workgroups"}
+    ri, rw = oracle.route(logits, k, **okw)
+    differ = np.any(gi != ri, axis=1) | np.any(gw.view(np.uint32) != rw.view(np.uint32), axis=1)
+    if differ.any():
+        scores = oracle.route_scores(logits, okw.get("gate", "sigmoid"), okw.get("bias"))
+        rule = {a: b for a, b in okw.items() if a not in ("gate", "bias")}
+        bad = invalid_tokens(gi, gw, ri, rw, scores, k=k, **rule)
+        say(f"  {int(differ.sum())} of {len(gi)} tokens not bit-identical; {len(bad)} invalid")
+        assert not bad, f"{len(bad)} invalid tokens, first: {bad[:3]}"
+
+
 def check(T, k, E, logits, **kw):
     say(f"route T={T} El={logits.shape[1]} k={k} E={E} "
         + " ".join(f"{a}={b}" for a, b in kw.items() if not isinstance(b, np.ndarray)))
     gi, gw = run_route(T, k, E, logits, **kw)
-    okw = {a: b for a, b in kw.items() if a != "num_workgroups"}
-    ri, rw = oracle.route(logits, k, **okw)
-    bad = np.nonzero(np.any(gi != ri, axis=1) | np.any(gw.view(np.uint32) != rw.view(np.uint32), axis=1))[0]
-    assert bad.size == 0, f"{bad.size} tokens differ, first {bad[:5]}: {gi[bad[0]]} {ri[bad[0]]} {gw[bad[0]]} {rw[bad[0]]}"
+    check_routing(gi, gw, logits, k, **kw)
     return gi, gw
 
 
@@ -197,8 +211,10 @@ def test_route_layout_builds_the_handle(name):
     say(f"route_layout {name}")
     ep.ep_route_layout(run.cfg, rt, logits, bias, ro, rs, idx, wts, run.h, run.ws)
     hnp = run.handle_np()
-    L = oracle.layout(w.topk_idx, w.E, w.R)
-    assert np.array_equal(idx.cpu().numpy(), w.topk_idx)
+    gi = idx.cpu().numpy()
+    check_routing(gi, wts.cpu().numpy(), x["logits"], w.k, bias=x.get("bias"),
+                  rep_offsets=x.get("rep_offsets"), rep_slots=x.get("rep_slots"), **r)
+    L = oracle.layout(gi, w.E, w.R)   # the layout of the device's own routing, bit for bit
     assert hnp["error_flag"][0] == 0
     assert np.array_equal(hnp["expert_counts"], L.expert_counts)
     assert np.array_equal(hnp["expert_offsets"], L.expert_offsets)
@@ -276,11 +292,10 @@ def test_route_layout_router_counted(T, El, k, G, TG, extra):
         kw["rep_slots"] = rng.permutation(E).astype(np.int32)
     R = 8 if E % 8 == 0 else 1
     say(f"route_layout counted T={T} El={El} k={k} E={E} R={R} G={G} TG={TG} {extra}")
-    ri, rw = oracle.route(z, k, **kw)
-    L = oracle.layout(ri, E, R)
     for nwg in (0, 7):
         gi, gw, h = route_layout(T, k, E, R, z, num_workgroups=nwg, **kw)
-        assert np.array_equal(gi, ri) and np.array_equal(gw.view(np.uint32), rw.view(np.uint32)), nwg
+        check_routing(gi, gw, z, k, **kw)
+        L = oracle.layout(gi, E, R)   # the layout of the device's own routing, bit for bit
         assert h["error_flag"][0] == 0, nwg
         for key in ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "src_of"):
             assert np.array_equal(h[key].reshape(-1), getattr(L, key).reshape(-1)), (nwg, key)
