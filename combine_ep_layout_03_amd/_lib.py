@@ -23,7 +23,8 @@ EP_GATE_SOFTMAX, EP_GATE_SIGMOID = 0, 1
 
 # Every symbol include/ep.h declares.
 EXPORTS = ("ep_abi_version", "ep_status_string", "ep_recv_capacity_rows",
-           "ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_layout_dispatch",
+           "ep_layout_workspace_bytes", "ep_layout", "ep_layout_noalloc", "ep_dispatch",
+           "ep_layout_dispatch",
            "ep_combine", "ep_combine_shared", "ep_combine_backward", "ep_silu_mul_quant",
            "ep_unpermute", "ep_route", "ep_route_layout")
 
@@ -79,6 +80,8 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.ep_layout_workspace_bytes.argtypes = [cfgp]
     L.ep_layout.restype = ctypes.c_int32
     L.ep_layout.argtypes = [cfgp, vp, hp, vp, vp]
+    L.ep_layout_noalloc.restype = ctypes.c_int32
+    L.ep_layout_noalloc.argtypes = [cfgp, vp, hp, vp]
     L.ep_dispatch.restype = ctypes.c_int32
     L.ep_dispatch.argtypes = [cfgp, hp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, vp]
     L.ep_layout_dispatch.restype = ctypes.c_int32
@@ -235,6 +238,12 @@ def _check_combine_buffers(c, recv_y, topk_weights, out, capacity_rows, out_rows
     _need(topk_weights, c.num_tokens * c.num_topk * 4, "topk_weights")
     rows = c.num_tokens if out_rows is None else out_rows
     _need(out, rows * c.hidden * 2, "out")
+
+
+def ep_layout_noalloc(cfg, topk_idx, handle, stream=None) -> None:
+    _check(load().ep_layout_noalloc(ctypes.byref(_cfg(cfg)), _ptr(topk_idx),
+                                    ctypes.byref(_handle(handle)), _stream(stream)),
+           "ep_layout_noalloc")
 
 
 def ep_dispatch(cfg, handle, topk_idx, x, recv_x, recv_scales, capacity_rows, stream=None) -> None:

@@ -155,6 +155,23 @@ ep_status ep_layout(const ep_config *cfg, const int32_t *topk_idx, const ep_layo
   return from_hip(ep::launch_layout(*cfg, plan, topk_idx, *h, workspace, stream));
 }
 
+ep_status ep_layout_noalloc(const ep_config *cfg, const int32_t *topk_idx, const ep_layout_t *h,
+                            hipStream_t stream) {
+  if (!config_ok(cfg) || !handle_ok(h) || !topk_idx) return EP_ERR_INVALID_ARG;
+  const ep::LayoutPlan plan =
+      ep::plan_layout((int64_t)cfg->num_tokens * cfg->num_topk, cfg->num_experts);
+  if (plan.workspace_bytes > ep::kLayoutScratchBytes) {
+    if (debug_enabled())
+      std::fprintf(stderr, "[ep] layout_noalloc: table of %zu bytes exceeds the %zu-byte array\n",
+                   plan.workspace_bytes, ep::kLayoutScratchBytes);
+    return EP_ERR_UNSUPPORTED;
+  }
+  void *scratch = nullptr;
+  if (ep::layout_scratch(&scratch) != hipSuccess) return EP_ERR_HIP;
+  trace("layout_noalloc", cfg);
+  return from_hip(ep::launch_layout(*cfg, plan, topk_idx, *h, scratch, stream));
+}
+
 ep_status ep_dispatch(const ep_config *cfg, const ep_layout_t *h, const int32_t *topk_idx,
                       const void *x, void *const *recv_x, float *const *recv_scales,
                       int64_t capacity_rows, hipStream_t stream) {

@@ -58,6 +58,12 @@ constexpr int kRouteCountStep = kRouteCountWaves * 4;  // tokens a router workgr
 constexpr int kRouteCountMaxExperts = 512;
 LayoutPlan plan_route_count(int64_t T, int k, int E);
 
+// The layout's chunk table in a file-scope device array (ep_layout_noalloc):
+// its size, and its address on the current device (resolved once per device).
+constexpr size_t kLayoutScratchBytes = 288 * 1024;
+constexpr int kMaxDevices = 64;
+hipError_t layout_scratch(void **ptr);
+
 // Launchers (no validation; the C ABI validates first).  Return hipError_t of
 // the launch.
 hipError_t launch_layout(const ep_config &c, const LayoutPlan &plan, const int32_t *topk_idx,

@@ -36,6 +36,8 @@
 // more in LDS atomics than the second launch.)  In ep_route_layout the router
 // writes that table itself (plan_route_count: one router workgroup per
 // chunk), and only the scatter kernel runs here.
+#include <mutex>
+
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -605,6 +607,41 @@ hipError_t launch_layout(const ep_config &c, const LayoutPlan &plan, const int32
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_layout_scatter(c, plan, topk_idx, h, workspace, s);
+}
+
+// ---- the layout without a caller workspace ------------------------------
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the chunk table lives in a file-scope device array instead of a
+// workspace argument.  Every GPU the library runs on holds its own copy until
+// the process ends; its address on the current device is resolved once per
+// device with hipGetSymbolAddress, and only that address is handed to the
+// kernels (the array's name is a host-side stand-in).  kLayoutScratchBytes
+// covers plan_layout's table for every valid config (its largest is 285 840
+// bytes, at E = 1984).  The count kernel writes every entry the scatter
+// kernel reads, so the array needs no clearing; calls that overlap on one
+// GPU share it and race.
+static __device__ __align__(256) int32_t scratch[kLayoutScratchBytes / sizeof(int32_t)];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t layout_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_layout_scatter(const ep_config &c, const LayoutPlan &plan,

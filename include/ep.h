@@ -192,6 +192,21 @@ ep_status ep_layout(const ep_config *cfg /*(host)*/, const int32_t *topk_idx,
                     const ep_layout_t *h /*(host struct of device pointers)*/,
                     void *workspace, hipStream_t stream);
 
+/* ep_layout without a workspace argument, for callers that cannot allocate
+ * device memory: code under hipGraph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments (minus `workspace`), results and
+ * errors as ep_layout.  The per-chunk table lives in a file-scope device
+ * array of 288 KiB, which covers every valid config (EP_ERR_UNSUPPORTED if a
+ * config ever needed more); each GPU the library runs on holds its own copy
+ * until the process ends.  The first call on a device resolves the array's
+ * address (hipGetSymbolAddress; make that first call outside a capture); no
+ * call allocates.  All calls on one GPU share the array: calls that overlap
+ * in time on one GPU (different streams, or concurrent host threads) race
+ * and must be serialized by the caller. */
+ep_status ep_layout_noalloc(const ep_config *cfg /*(host)*/, const int32_t *topk_idx,
+                            const ep_layout_t *h /*(host struct of device pointers)*/,
+                            hipStream_t stream);
+
 /* Dispatch ([DeepEP overview] "Pola penggunaan ...": route each token to its
  * top-k experts' ranks; [Perplexity blog] "Magntölun" for FP8).  For every
  * pair p = (t, j), with r = topk_idx[p] / (E/R) and row = slot_of[p] -

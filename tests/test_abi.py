@@ -277,3 +277,14 @@ def test_binding_checks_tensor_sizes():
         ep.ep_combine_backward(c, h, A, A, None, None, [A, A, A, small], None, 32, 0)
     with pytest.raises(ValueError, match=r"q_out\[2\]"):
         ep.ep_silu_mul_quant(c, h, 128, [A] * 4, [A, A, small, A], [A] * 4, 32, 0)
+
+
+def test_layout_noalloc_rejects_before_any_launch(lib):
+    c = ep.Config(16, 256, 2, 16, 4)
+    h = _lib.ep_layout_t(*([A] * 7))
+    for call in (lambda: ep.ep_layout_noalloc(c, None, h, 0),
+                 lambda: ep.ep_layout_noalloc(c, A, _lib.ep_layout_t(*([A] * 6 + [None])), 0),
+                 lambda: ep.ep_layout_noalloc(ep.Config(16, 256, 2, 15, 4), A, h, 0)):
+        with pytest.raises(ep.EpError) as ei:
+            call()
+        assert ei.value.status == ep.EP_ERR_INVALID_ARG
