@@ -8,16 +8,24 @@ the timed region; the expert stand-in (seeded bf16 rows in the receive
 buffers) is outside the path and is not timed.
 
 Prints ONE JSON line (rank 0, N=1):
-  value        = algorithmic bytes of a step / wall time of a step  [GB/s]
-  ms_per_step  = wall time over the K timed steps / K
+  value        = dispatch + combine algorithmic bytes / the mean of their
+                 summed HIP-event durations over the K back-to-back steps [GB/s]
+                 (the metric: dispatch + combine)
+  ms_per_step  = wall time of a whole step (layout, dispatch, combine) / K;
+                 step_GBps is the step's bytes over that time
   roofline     = the dominant kernel (combine): algorithmic bytes per launch /
                  its mean HIP-event duration, against 8 TB/s HBM peak
-  cpu_baseline = the CPU oracle (single thread) on a bounded sample
+  *_ceiling_GBps = same-run library ceilings (copy, fill, row scatter, row
+                 gather), steady state
   cache_flushed = layout / dispatch / combine medians with a 1 GiB read
                  before each step (cold caches), beside the back-to-back ones
   extras       = the other entry points timed in the same run (router, decode-
                  style steps, steps from the logits, shared-expert combine,
                  combine backward, SiLU re-quantization); --no-extras skips them
+  configs      = the other four workloads: per-call µs and GB/s, cold-cache
+                 medians and HIP-graph replays of the step; --no-configs skips
+  cpu_baseline = the CPU oracle (single thread) on the whole headline
+                 workload, each stage best of 3, with the host CPU model
 --summarize writes the profiles/ summaries from rocprofv3 CSV output.
 """
 from __future__ import annotations
@@ -96,39 +104,52 @@ def load_traffic(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(workload_name, sample_tokens, min_seconds):
-    """Time the CPU oracle (single thread) on the first `sample_tokens` tokens of
-    the workload, repeated until min_seconds of work; GB/s of algorithmic
-    bytes."""
-    import numpy as np
-    import oracle
-    from workloads import make_workload, make_expert_rows
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    w = make_workload(workload_name)
-    Ts = min(sample_tokens, w.T)
-    x, idx, wt = w.x[:Ts].copy(), w.topk_idx[:Ts].copy(), w.topk_w[:Ts].copy()
-    L0 = oracle.layout(idx, w.E, w.R)
-    y = make_expert_rows(Ts * w.k, w.H)
-    ys = [y[L0.rank_offsets[r]:L0.rank_offsets[r + 1]] for r in range(w.R)]
+
+def cpu_baseline(w, ybufs_host, reps=3):
+    """The CPU oracle, single-threaded, on the whole workload `w` (its tokens,
+    routing and the same expert rows as the GPU run): each stage timed
+    `reps` times, best kept.  value = dispatch + combine algorithmic bytes /
+    (best dispatch + best combine) in GB/s."""
+    import oracle
+
     oracle.lib()
-    times = []
-    t_end = time.perf_counter() + min_seconds
-    while len(times) < 2 or time.perf_counter() < t_end:
-        t0 = time.perf_counter()
-        L = oracle.layout(idx, w.E, w.R)
-        if w.fp8:
-            oracle.dispatch_fp8(x, idx, L)
-        else:
-            oracle.dispatch_bf16(x, idx, L)
-        oracle.combine(ys, idx, L, wt)
-        times.append(time.perf_counter() - t0)
-    b = algorithmic_bytes(Ts, w.H, w.k, w.E, w.R, w.fp8)
-    step_bytes = sum(b.values())
-    mean = statistics.mean(times)
-    return {"value": round(step_bytes / mean / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{workload_name} workload, first {Ts} of {w.T} tokens (layout + dispatch + "
-                      f"combine), {len(times)} repetitions, mean {mean:.3f} s each, single thread "
-                      f"of {os.cpu_count()} host cores"}
+    best = {}
+
+    def run(name, fn):
+        ts = []
+        out = None
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            out = fn()
+            ts.append(time.perf_counter() - t0)
+        best[name] = min(ts)
+        return out
+
+    L = run("layout", lambda: oracle.layout(w.topk_idx, w.E, w.R))
+    if w.fp8:
+        run("dispatch", lambda: oracle.dispatch_fp8(w.x, w.topk_idx, L))
+    else:
+        run("dispatch", lambda: oracle.dispatch_bf16(w.x, w.topk_idx, L))
+    run("combine", lambda: oracle.combine(ybufs_host, w.topk_idx, L, w.topk_w))
+    b = algorithmic_bytes(w.T, w.H, w.k, w.E, w.R, w.fp8)
+    dc_s = best["dispatch"] + best["combine"]
+    return {"value": round((b["dispatch"] + b["combine"]) / dc_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole {w.name} workload ({w.T} tokens, the GPU run's inputs and expert rows); "
+                      f"each stage best of {reps}; value = dispatch + combine bytes / their summed time; "
+                      f"one thread of {os.cpu_count()} host cores",
+            "stage_s": {k: round(v, 4) for k, v in best.items()},
+            "dc_s": round(dc_s, 4),
+            "cpu_model": cpu_model(), "host_cores": os.cpu_count()}
 
 
 # rocprofv3 kernel names ("ep::(anonymous namespace)::combine_kernel<false>(int const*, ...")
@@ -178,12 +199,12 @@ def summarize(trace_dir, fetch_dir, write_dir, workload, command_prefix):
     write_cal = per_kernel(write, CAL_FILL_KEY, False)  # KiB written by a CAL_BYTES-write kernel
     f_fetch = CAL_BYTES / fetch_cal
     f_write = CAL_BYTES / write_cal
-    cmd_trace = f"{command_prefix} rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o {workload} -- python3 bench.py --config {workload} --steps 20 --warmup 3 --skip-cpu"
+    cmd_trace = f"{command_prefix} rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o {workload} -- python3 bench.py --config {workload} --steps 20 --warmup 3 --skip-cpu --no-configs"
     lines = [f"# Kernel durations and HBM traffic, {workload} workload", "",
              "Kernel-trace command (run from the repository root):", "", "```", cmd_trace, "```", "",
              "Counter commands (one pass each):", "", "```",
-             f"{command_prefix} rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o {workload} -- python3 bench.py --config {workload} --steps 3 --warmup 1 --skip-cpu",
-             f"{command_prefix} rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o {workload} -- python3 bench.py --config {workload} --steps 3 --warmup 1 --skip-cpu",
+             f"{command_prefix} rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o {workload} -- python3 bench.py --config {workload} --steps 3 --warmup 1 --skip-cpu --no-configs",
+             f"{command_prefix} rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o {workload} -- python3 bench.py --config {workload} --steps 3 --warmup 1 --skip-cpu --no-configs",
              "```", "",
              f"Counter calibration: FETCH_SIZE of the elementwise copy kernel ({CAL_BYTES} B read) = "
              f"{fetch_cal:.0f} KiB, so FETCH bytes = FETCH_SIZE x {f_fetch:.4f}; WRITE_SIZE of the fill "
@@ -219,6 +240,257 @@ def summarize(trace_dir, fetch_dir, write_dir, workload, command_prefix):
     print(open(md).read())
 
 
+class Bench:
+    """Device state of one workload: inputs resident in HBM, the routing
+    handle, receive buffers, the expert stand-in rows (seeded N(0,1) bf16 in
+    the valid part of each rank buffer) and the prebuilt C arguments, so the
+    timed loops do no marshalling."""
+
+    def __init__(self, name, num_workgroups=0):
+        import numpy as np
+        import torch
+        import combine_ep_layout_03_amd as ep
+        from combine_ep_layout_03_amd import _lib
+        from combine_ep_layout_03_amd.buffers import Handle, RecvBuffers, alloc_workspace
+        from workloads import make_workload
+
+        self.torch = torch
+        self.L = L = ep.load()
+        dev = "cuda"
+        self.w = w = make_workload(name)
+        self.name = name
+        self.cfg = cfg = ep.Config(w.T, w.H, w.k, w.E, w.R, fp8=w.fp8, num_workgroups=num_workgroups)
+        self.cap = cap = ep.ep_recv_capacity_rows(cfg)
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
+        self.up = up
+        self.idx, self.x, self.wts = up(w.topk_idx), up(w.x), up(w.topk_w)
+        self.h = Handle.alloc(cfg, dev)
+        self.ws = alloc_workspace(cfg, dev)
+        self.recv = RecvBuffers.alloc(cfg, cap, device=dev)
+        self.out = torch.empty((w.T, w.H), dtype=torch.int16, device=dev)
+        ep.ep_layout(cfg, self.idx, self.h, self.ws)
+        torch.cuda.synchronize()
+        self.rank_counts = self.h.rank_counts.cpu().tolist()
+        self.gen = torch.Generator(device=dev)
+        self.gen.manual_seed(1)
+        self.ybufs = []
+        for r in range(w.R):
+            b = torch.zeros((cap, w.H), dtype=torch.int16, device=dev)
+            n = self.rank_counts[r]
+            if n:
+                b[:n] = torch.randn((n, w.H), generator=self.gen, device=dev).to(torch.bfloat16).view(torch.int16)
+            self.ybufs.append(b)
+        torch.cuda.synchronize()
+        self.ccfg = cfg.c()
+        self.ch = _lib.ep_layout_t(*[getattr(self.h, n).data_ptr() for n, _ in _lib.ep_layout_t._fields_])
+        self.stream = torch.cuda.current_stream()
+        self.sp = self.stream.cuda_stream
+        self.rx = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in self.recv.x])
+        self.rs = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in self.recv.scales]) if self.recv.scales else None
+        self.ry = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in self.ybufs])
+        self.pc, self.ph = ctypes.byref(self.ccfg), ctypes.byref(self.ch)
+        self.bytes = algorithmic_bytes(w.T, w.H, w.k, w.E, w.R, w.fp8)
+
+    def layout(self, sp=None):
+        st = self.L.ep_layout(self.pc, self.idx.data_ptr(), self.ph, self.ws.data_ptr(), sp or self.sp)
+        assert st == 0, st
+
+    def dispatch(self, sp=None):
+        st = self.L.ep_dispatch(self.pc, self.ph, self.idx.data_ptr(), self.x.data_ptr(), self.rx, self.rs,
+                                self.cap, sp or self.sp)
+        assert st == 0, st
+
+    def combine(self, sp=None):
+        st = self.L.ep_combine(self.pc, self.ph, self.idx.data_ptr(), self.ry, self.wts.data_ptr(),
+                               self.out.data_ptr(), self.cap, sp or self.sp)
+        assert st == 0, st
+
+    def layout_dispatch(self, sp=None):
+        st = self.L.ep_layout_dispatch(self.pc, self.idx.data_ptr(), self.ph, self.ws.data_ptr(),
+                                       self.x.data_ptr(), self.rx, self.rs, self.cap, sp or self.sp)
+        assert st == 0, st
+
+    def check_ok(self):
+        assert int(self.h.error_flag.item()) == 0
+
+    def time_steps(self, K, warmup):
+        """K back-to-back steps (layout, dispatch, combine), HIP events on the
+        stream between the calls; wall time with a synchronize on both sides."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.layout(); self.dispatch(); self.combine()
+        torch.cuda.synchronize()
+        self.check_ok()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e in ev:
+            e[0].record(self.stream)
+            self.layout()
+            e[1].record(self.stream)
+            self.dispatch()
+            e[2].record(self.stream)
+            self.combine()
+            e[3].record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        self.check_ok()
+        lay = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+        dis = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+        com = [e[2].elapsed_time(e[3]) * 1e3 for e in ev]
+        return dict(layout=lay, dispatch=dis, combine=com, dc=[a + b for a, b in zip(dis, com)], wall=wall)
+
+    def time_cold(self, reps):
+        """The same three calls with cold caches: a 1 GiB read before each step
+        (4x the 256 MB MALL, 32x the L2; a read, so it leaves no dirty lines
+        whose write-back would land in the timed kernels), outside the events."""
+        torch = self.torch
+        flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+        for e in fev:
+            flush_buf.view(torch.int64).sum()
+            e[0].record(self.stream)
+            self.layout()
+            e[1].record(self.stream)
+            self.dispatch()
+            e[2].record(self.stream)
+            self.combine()
+            e[3].record(self.stream)
+        torch.cuda.synchronize()
+        del flush_buf
+        self.check_ok()
+        return {name: round(statistics.median(e[a].elapsed_time(e[a + 1]) * 1e3 for e in fev), 2)
+                for a, name in enumerate(("layout_us", "dispatch_us", "combine_us"))}
+
+    def time_graph(self, fns, K, warmup):
+        """µs per replay of the calls captured once in a HIP graph."""
+        torch = self.torch
+        gs = torch.cuda.Stream()
+        gs.wait_stream(self.stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g, stream=gs):
+                for fn in fns:
+                    fn(gs.cuda_stream)
+        self.stream.wait_stream(gs)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(K):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        self.check_ok()
+        return a.elapsed_time(b) * 1e3 / K
+
+    def free(self):
+        for n in ("idx", "x", "wts", "h", "ws", "recv", "out", "ybufs"):
+            setattr(self, n, None)
+        self.torch.cuda.empty_cache()
+
+
+def stats_of(bench, t):
+    """Per-call medians, means and GB/s of algorithmic bytes from time_steps."""
+    b = bench.bytes
+    med = {k: statistics.median(v) for k, v in t.items() if k != "wall"}
+    mean = {k: statistics.mean(v) for k, v in t.items() if k != "wall"}
+    dc_bytes = b["dispatch"] + b["combine"]
+    return {
+        "layout_us": round(med["layout"], 2), "dispatch_us": round(med["dispatch"], 2),
+        "combine_us": round(med["combine"], 2), "dc_us": round(med["dc"], 2),
+        "dc_us_mean": round(mean["dc"], 2),
+        "dispatch_GBps": round(b["dispatch"] / (med["dispatch"] * 1e-6) / 1e9, 1),
+        "combine_GBps": round(b["combine"] / (med["combine"] * 1e-6) / 1e9, 1),
+        "dc_GBps": round(dc_bytes / (med["dc"] * 1e-6) / 1e9, 1),
+        "dc_frac_of_peak": round(dc_bytes / (med["dc"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+    }
+
+
+def library_ceilings(bench, reps=3):
+    """Same-run practical ceilings from library kernels (torch), each timed as
+    `reps` back-to-back repetitions so that write-backs a call leaves in the
+    caches are paid inside the timed window (steady state):
+      copy     torch.bitwise_not over 1 GiB (reads 1 GiB, writes 1 GiB);
+      write    torch fill_ of 1 GiB;
+      scatter  dispatch's write pattern: torch index_copy_ of the T token rows
+               (H bytes each, as int64) into their k slot rows of one [T*k, H]
+               buffer, one call per top-k slot j (reads T*H, writes T*H per
+               call);
+      gather   combine's read pattern: torch index_select of the T*k expert
+               rows (bf16, slot order) into pair order (reads and writes
+               T*k*2H).
+    GB/s = bytes the operation moves / time."""
+    torch = bench.torch
+    w = bench.w
+
+    def steady(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / n
+
+    out = {}
+    src = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    out["copy_ceiling_GBps"] = round(2 * CAL_BYTES / steady(lambda: torch.bitwise_not(src, out=dst), 5) / 1e9, 1)
+    out["write_ceiling_GBps"] = round(CAL_BYTES / steady(lambda: src.fill_(1), 5) / 1e9, 1)
+    del src, dst
+    P, H = w.T * w.k, w.H
+    slot = bench.h.slot_of.view(w.T, w.k).long()
+    cols = [slot[:, j].contiguous() for j in range(w.k)]
+    rowq = H // 8 if H % 8 == 0 else None
+    if rowq:
+        q64 = torch.randint(0, 1 << 62, (w.T, rowq), dtype=torch.int64, device="cuda")
+        d64 = torch.empty((P, rowq), dtype=torch.int64, device="cuda")
+
+        def scatter():
+            for j in range(w.k):
+                d64.index_copy_(0, cols[j], q64)
+        t = steady(scatter, reps)
+        out["scatter_ceiling_GBps"] = round(2 * P * H / t / 1e9, 1)
+        del q64, d64
+    ycat = torch.cat([bench.ybufs[r][:bench.rank_counts[r]] for r in range(w.R)]).view(torch.int64)
+    sel = torch.empty_like(ycat)
+    order = bench.h.slot_of.long()
+    t = steady(lambda: torch.index_select(ycat, 0, order, out=sel), reps)
+    out["gather_ceiling_GBps"] = round(2 * P * 2 * H / t / 1e9, 1)
+    del ycat, sel
+    torch.cuda.empty_cache()
+    out["ceiling_definitions"] = ("library kernels, steady state (back-to-back repetitions): copy = "
+                                  "torch.bitwise_not 1 GiB; write = fill_ 1 GiB; scatter = index_copy_ "
+                                  "of the token rows into their k slot rows (dispatch's write pattern); "
+                                  "gather = index_select of the expert rows into pair order (combine's "
+                                  "read pattern); GB/s = bytes moved / time")
+    return out
+
+
+def config_summary(name, K, warmup):
+    """One line of the configs block: per-call medians and GB/s for layout,
+    dispatch and combine on workload `name`, cold-cache medians, and the step
+    replayed from a HIP graph (layout + dispatch + combine, and the one-call
+    layout + dispatch + combine)."""
+    b = Bench(name)
+    try:
+        t = b.time_steps(K, warmup)
+        res = {"T": b.w.T, "hidden": b.w.H, "top_k": b.w.k, "experts": b.w.E, "ranks": b.w.R,
+               "dispatch": "fp8_e4m3" if b.w.fp8 else "bf16", **stats_of(b, t),
+               "step_us": round(t["wall"] / K * 1e6, 2),
+               "cache_flushed": b.time_cold(min(K, 20))}
+        res["graph_step_us"] = round(b.time_graph([b.layout, b.dispatch, b.combine], K, warmup), 2)
+        res["graph_fused_step_us"] = round(b.time_graph([b.layout_dispatch, b.combine], K, warmup), 2)
+        return res
+    finally:
+        b.free()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,11 +498,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="v3")
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU-oracle baseline")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--no-extras", action="store_true",
                     help="skip timing the other entry points (router, decode-style, backward, expert-side)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads' lines (the configs block)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph and replayed")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -254,167 +526,61 @@ def main():
         epbuild.build()
     import combine_ep_layout_03_amd as ep
     from combine_ep_layout_03_amd import _lib
-    from combine_ep_layout_03_amd.buffers import Handle, RecvBuffers, alloc_workspace
-    from workloads import CONFIGS, make_workload
-
-    L = ep.load()
-    dev = "cuda"
-    w = make_workload(args.config)
-    cfg = ep.Config(w.T, w.H, w.k, w.E, w.R, fp8=w.fp8, num_workgroups=args.num_workgroups)
-    cap = ep.ep_recv_capacity_rows(cfg)
-    up = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
-    idx, x, wts = up(w.topk_idx), up(w.x), up(w.topk_w)
-    h = Handle.alloc(cfg, dev)
-    ws = alloc_workspace(cfg, dev)
-    recv = RecvBuffers.alloc(cfg, cap, device=dev)
-    out = torch.empty((w.T, w.H), dtype=torch.int16, device=dev)
-
-    # layout once to size the expert stand-in rows: seeded N(0,1) bf16 rows in
-    # the valid part of each rank buffer
-    ep.ep_layout(cfg, idx, h, ws)
-    torch.cuda.synchronize()
-    rank_counts = h.rank_counts.cpu().tolist()
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(1)
-    ybufs = []
-    for r in range(w.R):
-        b = torch.zeros((cap, w.H), dtype=torch.int16, device=dev)
-        n = rank_counts[r]
-        if n:
-            b[:n] = torch.randn((n, w.H), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
-        ybufs.append(b)
-    torch.cuda.synchronize()
-
-    # prebuilt C arguments for the timed loop (no per-call marshalling)
-    ccfg = cfg.c()
-    ch = _lib.ep_layout_t(*[getattr(h, n).data_ptr() for n, _ in _lib.ep_layout_t._fields_])
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
-    rx = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in recv.x])
-    rs = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in recv.scales]) if recv.scales else None
-    ry = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in ybufs])
-    pc, ph = ctypes.byref(ccfg), ctypes.byref(ch)
-
-    def layout():
-        st = L.ep_layout(pc, idx.data_ptr(), ph, ws.data_ptr(), sp)
-        assert st == 0, st
-
-    def dispatch():
-        st = L.ep_dispatch(pc, ph, idx.data_ptr(), x.data_ptr(), rx, rs, cap, sp)
-        assert st == 0, st
-
-    def combine():
-        st = L.ep_combine(pc, ph, idx.data_ptr(), ry, wts.data_ptr(), out.data_ptr(), cap, sp)
-        assert st == 0, st
-
-    # Plain streaming kernels of known size, same run: an elementwise pass that
-    # reads 1 GiB and writes 1 GiB (the copy ceiling) and a 1 GiB fill (the
-    # write ceiling).  They are also the calibration kernels for the HBM byte
-    # counters (see --summarize).
-    src = torch.empty(CAL_BYTES, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def timed(fn, reps=5):
-        ms = []
-        for _ in range(reps):
-            e0.record()
-            fn()
-            e1.record()
-            e1.synchronize()
-            ms.append(e0.elapsed_time(e1))
-        return statistics.median(ms)
-
-    fill_ms = timed(lambda: src.fill_(1))
-    copy_ms = timed(lambda: torch.bitwise_not(src, out=dst))
-    copy_gbps = 2 * CAL_BYTES / (copy_ms * 1e-3) / 1e9
-    write_gbps = CAL_BYTES / (fill_ms * 1e-3) / 1e9
-    del src, dst
-
-    for _ in range(args.warmup):
-        layout(); dispatch(); combine()
-    torch.cuda.synchronize()
-    assert int(h.error_flag.item()) == 0
+    from combine_ep_layout_03_amd.buffers import Handle, alloc_workspace
+    from workloads import CONFIGS
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        e = ev[i]
-        e[0].record(stream)
-        layout()
-        e[1].record(stream)
-        dispatch()
-        e[2].record(stream)
-        combine()
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    assert int(h.error_flag.item()) == 0
+    bench = Bench(args.config, args.num_workgroups)
+    w, L, cap, sp = bench.w, bench.L, bench.cap, bench.sp
+    pc, ph = bench.pc, bench.ph
+    idx, x, wts, ws, out = bench.idx, bench.x, bench.wts, bench.ws, bench.out
+    rx, rs, ry = bench.rx, bench.rs, bench.ry
+    ceil = library_ceilings(bench)
 
-    lay = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
-    dis = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
-    com = [e[2].elapsed_time(e[3]) * 1e3 for e in ev]
-    dc = [a + b for a, b in zip(dis, com)]
-    b = algorithmic_bytes(w.T, w.H, w.k, w.E, w.R, w.fp8)
+    t = bench.time_steps(K, args.warmup)
+    st = stats_of(bench, t)
+    b = bench.bytes
     step_bytes = sum(b.values())
-    ms_per_step = wall / K * 1e3
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    mean_com = statistics.mean(com)
+    ms_per_step = t["wall"] / K * 1e3
+    mean_com = statistics.mean(t["combine"])
     achieved = b["combine"] / (mean_com * 1e-6) / 1e9
+    dc_bytes = b["dispatch"] + b["combine"]
+    value = dc_bytes / (statistics.mean(t["dc"]) * 1e-6) / 1e9
 
     def pct(v, q):
-        s = sorted(v)
-        return round(s[min(len(s) - 1, int(q * len(s)))], 2)
+        s_ = sorted(v)
+        return round(s_[min(len(s_) - 1, int(q * len(s_)))], 2)
 
-    # The same three calls with cold caches: before each step a 1 GiB read
-    # (4x the 256 MB MALL, 32x the L2; a read, so it leaves no dirty lines
-    # whose write-back would land in the timed kernels) runs outside the
-    # kernel events.  The timed loop above is back-to-back steps, as in a
-    # layer loop that reuses its buffers.
-    flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
-    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(min(K, 20))]
-    for e in fev:
-        flush_buf.view(torch.int64).sum()
-        e[0].record(stream)
-        layout()
-        e[1].record(stream)
-        dispatch()
-        e[2].record(stream)
-        combine()
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    del flush_buf
-    assert int(h.error_flag.item()) == 0
-    flushed = {name: round(statistics.median(e[a].elapsed_time(e[a + 1]) * 1e3 for e in fev), 2)
-               for a, name in enumerate(("layout_us", "dispatch_us", "combine_us"))}
+    flushed = bench.time_cold(min(K, 20))
 
     extras = None
     if not args.no_extras:
         # the other entry points on the same handle and buffers: combine with a
         # shared-expert row, and the backward of combine (gradient rows + grad_w)
+        gen = bench.gen
+        rank_counts = bench.rank_counts
+        up = bench.up
         gen.manual_seed(2)
-        shared = torch.randn((w.T, w.H), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
-        gout = torch.randn((w.T, w.H), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
-        grows = [torch.empty((cap, w.H), dtype=torch.int16, device=dev) for _ in range(w.R)]
-        gwt = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
-        rgp = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in grows])
+        shared = torch.randn((w.T, w.H), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+        gout = torch.randn((w.T, w.H), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+        grows = [torch.empty((cap, w.H), dtype=torch.int16, device="cuda") for _ in range(w.R)]
+        gwt = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
+        rgp = (ctypes.c_void_p * w.R)(*[t_.data_ptr() for t_ in grows])
         xb = extra_bytes(w.T, w.H, w.k)
         # expert GEMM-1 outputs (gate | up, 2*EXPERT_I bf16) in the receive
         # layout: capacity-sized buffers, seeded rows in the valid part
         act, aq, asc = [], [], []
         for r in range(w.R):
-            a = torch.zeros((cap, 2 * EXPERT_I), dtype=torch.int16, device=dev)
+            a = torch.zeros((cap, 2 * EXPERT_I), dtype=torch.int16, device="cuda")
             if rank_counts[r]:
                 a[:rank_counts[r]] = torch.randn((rank_counts[r], 2 * EXPERT_I), generator=gen,
-                                                 device=dev).to(torch.bfloat16).view(torch.int16)
+                                                 device="cuda").to(torch.bfloat16).view(torch.int16)
             act.append(a)
-            aq.append(torch.empty((cap, EXPERT_I), dtype=torch.uint8, device=dev))
-            asc.append(torch.empty((cap, EXPERT_I // 128), dtype=torch.float32, device=dev))
-        pa = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in act])
-        pq = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in aq])
-        ps = (ctypes.c_void_p * w.R)(*[t.data_ptr() for t in asc])
+            aq.append(torch.empty((cap, EXPERT_I), dtype=torch.uint8, device="cuda"))
+            asc.append(torch.empty((cap, EXPERT_I // 128), dtype=torch.float32, device="cuda"))
+        pa = (ctypes.c_void_p * w.R)(*[t_.data_ptr() for t_ in act])
+        pq = (ctypes.c_void_p * w.R)(*[t_.data_ptr() for t_ in aq])
+        ps = (ctypes.c_void_p * w.R)(*[t_.data_ptr() for t_ in asc])
         calls = {
             "silu_mul_quant": lambda: L.ep_silu_mul_quant(pc, ph, EXPERT_I, pa, pq, ps, cap, sp),
             "combine_shared": lambda: L.ep_combine_shared(pc, ph, idx.data_ptr(), ry, wts.data_ptr(),
@@ -430,14 +596,14 @@ def main():
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(min(K, 20))]
             for a, b_ in evs:
-                a.record(stream)
+                a.record(bench.stream)
                 assert fn() == 0
-                b_.record(stream)
+                b_.record(bench.stream)
             torch.cuda.synchronize()
             us = statistics.median(a.elapsed_time(b_) * 1e3 for a, b_ in evs)
             extras[name] = {"us": round(us, 2), "algorithmic_bytes": xb[name],
                             "GBps": round(xb[name] / (us * 1e-6) / 1e9, 1)}
-        assert int(h.error_flag.item()) == 0
+        bench.check_ok()
         del shared, gout, grows, gwt, act, aq, asc
 
         # the router on this workload's logits, into buffers of its own: alone,
@@ -448,12 +614,12 @@ def main():
         logits_d = up(rin["logits"])
         opt = lambda key: up(rin[key]) if key in rin else None
         bias_d, ro_d, rsl_d = opt("bias"), opt("rep_offsets"), opt("rep_slots")
-        dp = lambda t: None if t is None else t.data_ptr()
+        dp = lambda t_: None if t_ is None else t_.data_ptr()
         crt = ep.Router(El, **rin["router"]).c()
         prt = ctypes.byref(crt)
         idx2, w2 = torch.empty_like(idx), torch.empty_like(wts)
-        h2 = Handle.alloc(cfg, dev)
-        ws2 = alloc_workspace(cfg, dev)
+        h2 = Handle.alloc(bench.cfg, "cuda")
+        ws2 = alloc_workspace(bench.cfg, "cuda")
         ch2 = _lib.ep_layout_t(*[getattr(h2, n).data_ptr() for n, _ in _lib.ep_layout_t._fields_])
         ph2 = ctypes.byref(ch2)
         rt_args = (pc, prt, logits_d.data_ptr(), dp(bias_d), dp(ro_d), dp(rsl_d), idx2.data_ptr(),
@@ -463,22 +629,23 @@ def main():
         route_bytes = (w.T * El * 4 + w.T * w.k * 8 + (El * 4 if bias_d is not None else 0)
                        + (w.T * w.k * 8 if ro_d is not None else 0))
         for name, fn, nbytes in (("route", rcall, route_bytes),
-                                 ("route_layout", rlcall, route_bytes + algorithmic_bytes(
-                                     w.T, w.H, w.k, w.E, w.R, w.fp8)["layout"])):
+                                 ("route_layout", rlcall, route_bytes + b["layout"])):
             for _ in range(3):
                 assert fn() == 0
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(min(K, 20))]
             for a, b_ in evs:
-                a.record(stream)
+                a.record(bench.stream)
                 assert fn() == 0
-                b_.record(stream)
+                b_.record(bench.stream)
             torch.cuda.synchronize()
             us = statistics.median(a.elapsed_time(b_) * 1e3 for a, b_ in evs)
             extras[name] = {"us": round(us, 2), "algorithmic_bytes": nbytes,
                             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
         assert int(h2.error_flag.item()) == 0
-        assert torch.equal(idx2, idx) and torch.equal(h2.slot_of, h.slot_of)
+        # the router's picks may differ from the generator's only at near ties
+        # (tests/router_validity.py); the bench only needs a valid handle
+        assert int(h2.rank_offsets[-1].item()) == w.T * w.k
 
         # decode-style steps: the one-call layout + dispatch, and the cached-
         # handle step (gating unchanged: dispatch + combine, no layout)
@@ -489,11 +656,11 @@ def main():
             torch.cuda.synchronize()
             a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             n = max(K, 20)
-            a.record(stream)
+            a.record(bench.stream)
             for _ in range(n):
                 for fn in fns:
                     assert fn() == 0
-            b_.record(stream)
+            b_.record(bench.stream)
             torch.cuda.synchronize()
             return a.elapsed_time(b_) * 1e3 / n
 
@@ -501,6 +668,8 @@ def main():
                                           cap, sp)
         cd = lambda: L.ep_dispatch(pc, ph, idx.data_ptr(), x.data_ptr(), rx, rs, cap, sp)
         cc = lambda: L.ep_combine(pc, ph, idx.data_ptr(), ry, wts.data_ptr(), out.data_ptr(), cap, sp)
+        lna = lambda: L.ep_layout_noalloc(pc, idx.data_ptr(), ph, sp)
+        extras["layout_noalloc_us"] = round(step_time([lna]), 2)
         extras["layout_dispatch_us"] = round(step_time([ld]), 2)
         extras["fused_step_us"] = round(step_time([ld, cc]), 2)
         extras["cached_handle_step_us"] = round(step_time([cd, cc]), 2)
@@ -513,57 +682,33 @@ def main():
                                            rs, cap, sp)
         extras["routed_fused_step_us"] = round(step_time([rcall, rld, rc]), 2)
         assert int(h2.error_flag.item()) == 0
-        assert int(h.error_flag.item()) == 0
+        bench.check_ok()
 
-    graph_us = None
-    fused_graph_us = None
+    graph_us = fused_graph_us = None
     if args.graph:
-        # one step (layout + dispatch + combine) captured once, replayed K times
-        gs = torch.cuda.Stream()
-        gs.wait_stream(stream)
-        g = torch.cuda.CUDAGraph()
-        gsp = gs.cuda_stream
-        with torch.cuda.stream(gs):
-            with torch.cuda.graph(g, stream=gs):
-                assert L.ep_layout(pc, idx.data_ptr(), ph, ws.data_ptr(), gsp) == 0
-                assert L.ep_dispatch(pc, ph, idx.data_ptr(), x.data_ptr(), rx, rs, cap, gsp) == 0
-                assert L.ep_combine(pc, ph, idx.data_ptr(), ry, wts.data_ptr(), out.data_ptr(), cap, gsp) == 0
-        stream.wait_stream(gs)
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ga.record()
-        for _ in range(K):
-            g.replay()
-        gb.record()
-        torch.cuda.synchronize()
-        graph_us = ga.elapsed_time(gb) * 1e3 / K
-        assert int(h.error_flag.item()) == 0
-        # the fused step (ep_layout_dispatch + ep_combine) as a graph
-        g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(gs):
-            with torch.cuda.graph(g2, stream=gs):
-                assert L.ep_layout_dispatch(pc, idx.data_ptr(), ph, ws.data_ptr(), x.data_ptr(), rx,
-                                            rs, cap, gsp) == 0
-                assert L.ep_combine(pc, ph, idx.data_ptr(), ry, wts.data_ptr(), out.data_ptr(), cap,
-                                    gsp) == 0
-        stream.wait_stream(gs)
-        for _ in range(args.warmup):
-            g2.replay()
-        torch.cuda.synchronize()
-        ga.record()
-        for _ in range(K):
-            g2.replay()
-        gb.record()
-        torch.cuda.synchronize()
-        fused_graph_us = ga.elapsed_time(gb) * 1e3 / K
-        assert int(h.error_flag.item()) == 0
+        graph_us = round(bench.time_graph([bench.layout, bench.dispatch, bench.combine], K, args.warmup), 2)
+        fused_graph_us = round(bench.time_graph([bench.layout_dispatch, bench.combine], K, args.warmup), 2)
+
+    cpu = None
+    if not args.skip_cpu:
+        yh = [bench.ybufs[r][:bench.rank_counts[r]].cpu().numpy().view(np.uint16) for r in range(w.R)]
+        cpu = cpu_baseline(w, yh)
+        del yh
+
+    configs = None
+    if not args.no_configs:
+        bench.free()
+        configs = {}
+        for name in CONFIGS:
+            if name != args.config:
+                configs[name] = config_summary(name, max(20, min(K, 50)), args.warmup)
 
     res = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
+        "value_definition": "dispatch + combine algorithmic bytes / mean (dispatch + combine) HIP-event "
+                            "time over the timed steps",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
@@ -571,7 +716,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": ("fp8_e4m3 dispatch (fp32 per-128 scales) / bf16 combine, fp32 accumulate" if w.fp8
+                  else "bf16 dispatch / bf16 combine, fp32 accumulate"),
         "data": "synthetic (seeded: x ~ N(0,1) bf16, router logits N(0,1); expert outputs N(0,1) bf16)",
         "config": {"workload": args.config, "T": w.T, "hidden": w.H, "top_k": w.k,
                    "experts": w.E, "ranks": w.R,
@@ -581,25 +727,21 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": load_traffic("combine", args.config),
                      "algorithmic_bytes_per_launch": b["combine"], "mean_launch_us": round(mean_com, 2)},
-        "layout_us": round(statistics.median(lay), 2),
-        "dispatch_us": round(statistics.median(dis), 2),
-        "combine_us": round(statistics.median(com), 2),
-        "dc_us": round(statistics.median(dc), 2),
-        "dc_us_p10_p90": [pct(dc, 0.1), pct(dc, 0.9)],
-        "dc_GBps": round((b["dispatch"] + b["combine"]) / (statistics.median(dc) * 1e-6) / 1e9, 1),
-        "dispatch_GBps": round(b["dispatch"] / (statistics.median(dis) * 1e-6) / 1e9, 1),
-        "combine_GBps": round(b["combine"] / (statistics.median(com) * 1e-6) / 1e9, 1),
+        **st,
+        "dc_us_p10_p90": [pct(t["dc"], 0.1), pct(t["dc"], 0.9)],
+        "dc_bytes": dc_bytes,
+        "step_bytes": step_bytes,
+        "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "cache_flushed": flushed,
-        "copy_ceiling_GBps": round(copy_gbps, 1),
-        "write_ceiling_GBps": round(write_gbps, 1),
-        "bytes_per_step": step_bytes,
-        "graph_step_us": None if graph_us is None else round(graph_us, 2),
-        "fused_graph_step_us": None if fused_graph_us is None else round(fused_graph_us, 2),
+        **ceil,
+        "dispatch_frac_of_scatter_ceiling": (round(st["dispatch_GBps"] / ceil["scatter_ceiling_GBps"], 3)
+                                             if "scatter_ceiling_GBps" in ceil else None),
+        "graph_step_us": graph_us,
+        "fused_graph_step_us": fused_graph_us,
         "extras": extras,
-        "cpu_baseline": None,
+        "configs": configs,
+        "cpu_baseline": cpu,
     }
-    if not args.skip_cpu:
-        res["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample_tokens, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
