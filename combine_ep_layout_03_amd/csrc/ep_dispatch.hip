@@ -14,7 +14,8 @@
 // once and, for FP8, quantized once; lanes 0..k-1 resolve the k destination
 // rows and their base addresses are taken with readlane, so each of the k
 // copies is a scalar-base + vector-offset 16-byte non-temporal store.
-//   BF16: a segment is 64 chunks of 16 B (512 channels), one chunk per lane.
+//   BF16: a segment is 128 chunks of 16 B (1024 channels), two chunks per lane
+//         (c and c + 64), both loaded before the k copies are stored.
 //   FP8:  a segment is 8 blocks of 128 channels; a lane holds 16 channels
 //         (2 x 16 B of bf16 -> 16 B of E4M3), so 8 lanes form one block and
 //         the block amax takes 3 xor-shuffles.  amax is taken on the bf16 bit
@@ -25,7 +26,10 @@
 // (Measured on MI355X at T=8192, H=7168, k=8: one-wave units beat one wave per
 // token, four-wave workgroups, token-per-workgroup with LDS-staged scales,
 // copy-per-wave splits and plain stores; the scattered row stores, not the
-// quantization arithmetic, bound this kernel.)
+// quantization arithmetic, bound this kernel.  Plain stores look faster per
+// call but leave dirty lines in the MALL whose write-back the next kernel
+// pays: slower in steady state.  BF16 at T=4096, H=2048, k=6: two chunks per
+// lane take 1.5 us off one chunk, four add it back.)
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -36,6 +40,7 @@ using namespace dev;
 
 constexpr int kThreads = kRowWaves * kWave;
 constexpr int kFp8SegBlocks = 8;  // 128-channel blocks per FP8 work unit (= 64 lanes x 16 ch)
+constexpr int kBf16SegChunks = 2 * kWave;  // 16-byte chunks per BF16 work unit (two per lane)
 
 // Lane j < k: byte address of token t's destination row j (0 if unusable,
 // which also raises EP_DEVERR_ROW).  `rowbytes` is the destination row pitch.
@@ -67,12 +72,13 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
   if (*err != 0) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int nch = H / 8;  // 16-byte chunks per row
-  const int nseg = (nch + kWave - 1) / kWave;
+  const int nseg = (nch + kBf16SegChunks - 1) / kBf16SegChunks;
   const int64_t units = (int64_t)T * nseg;
   for (int64_t u = (int64_t)blockIdx.x * kRowWaves + wave; u < units;
        u += (int64_t)gridDim.x * kRowWaves) {
     const int64_t t = u / nseg;
-    const int c = (int)(u % nseg) * kWave + lane;
+    const int c0 = (int)(u % nseg) * kBf16SegChunks + lane;
+    const int c1 = c0 + kWave;
     uint64_t dst = 0;
     if (lane < k) {
       int32_t r;
@@ -81,12 +87,15 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
                      (const void *const *)rx.p, (int64_t)H * 2, r, row);
     }
     if (__ballot(lane < k && dst == 0) != 0) continue;  // a bad row: write nothing for t
-    const bool ok = c < nch;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (ok) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + t * H) + c);
+    const bool ok0 = c0 < nch, ok1 = c1 < nch;
+    const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + t * H);
+    u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+    if (ok0) v0 = __builtin_nontemporal_load(xrow + c0);
+    if (ok1) v1 = __builtin_nontemporal_load(xrow + c1);
     for (int j = 0; j < k; ++j) {
       u32x4 *d = reinterpret_cast<u32x4 *>(readlane64(dst, j));
-      if (ok) __builtin_nontemporal_store(v, d + c);
+      if (ok0) __builtin_nontemporal_store(v0, d + c0);
+      if (ok1) __builtin_nontemporal_store(v1, d + c1);
     }
   }
 }
@@ -150,7 +159,7 @@ hipError_t launch_dispatch(const ep_config &c, const ep_layout_t &h, const int32
                        h.error_flag, c.num_tokens, c.hidden, c.num_topk, c.num_experts, El,
                        capacity_rows, rx, rs);
   } else {
-    const int64_t nseg = (c.hidden / 8 + kWave - 1) / kWave;
+    const int64_t nseg = (c.hidden / 8 + kBf16SegChunks - 1) / kBf16SegChunks;
     const int grid = row_grid(c, (int64_t)c.num_tokens * nseg);
     hipLaunchKernelGGL(dispatch_bf16_kernel, dim3(grid), dim3(kThreads), 0, s,
                        static_cast<const uint16_t *>(x), topk_idx, h.slot_of, h.rank_offsets,
