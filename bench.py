@@ -380,6 +380,22 @@ class Bench:
         self.check_ok()
         return a.elapsed_time(b) * 1e3 / K
 
+    def time_loop(self, fn, K):
+        """µs per call of `fn` over K calls back to back (events around the
+        loop only)."""
+        torch = self.torch
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for _ in range(K):
+            fn()
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        self.check_ok()
+        return a.elapsed_time(b) * 1e3 / K
+
     def time_cold(self, reps):
         """The same three calls with cold caches: a 1 GiB read before each step
         (4x the 256 MB MALL, 32x the L2; a read, so it leaves no dirty lines
@@ -448,7 +464,7 @@ def stats_of(bench, t):
     }
 
 
-def library_ceilings(bench, reps=3):
+def library_ceilings(bench, reps=8):
     """Same-run practical ceilings from library kernels (torch), each timed as
     `reps` back-to-back repetitions so that write-backs a call leaves in the
     caches are paid inside the timed window (steady state):
@@ -480,8 +496,8 @@ def library_ceilings(bench, reps=3):
     out = {}
     src = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
-    out["copy_ceiling_GBps"] = round(2 * CAL_BYTES / steady(lambda: torch.bitwise_not(src, out=dst), 5) / 1e9, 1)
-    out["write_ceiling_GBps"] = round(CAL_BYTES / steady(lambda: src.fill_(1), 5) / 1e9, 1)
+    out["copy_ceiling_GBps"] = round(2 * CAL_BYTES / steady(lambda: torch.bitwise_not(src, out=dst), reps) / 1e9, 1)
+    out["write_ceiling_GBps"] = round(CAL_BYTES / steady(lambda: src.fill_(1), reps) / 1e9, 1)
     del src, dst
     P, H = w.T * w.k, w.H
     slot = bench.h.slot_of.view(w.T, w.k).long()
@@ -508,7 +524,8 @@ def library_ceilings(bench, reps=3):
                                   "torch.bitwise_not 1 GiB; write = fill_ 1 GiB; scatter = index_copy_ "
                                   "of the token rows into their k slot rows (dispatch's write pattern); "
                                   "gather = index_select of the expert rows into pair order (combine's "
-                                  "read pattern); GB/s = bytes moved / time")
+                                  "read pattern); GB/s = bytes moved / time; compared with dispatch "
+                                  "and combine timed the same way (back to back)")
     return out
 
 
@@ -590,6 +607,10 @@ def main():
     # numbers are an upper bound)
     step_us, wall = bench.time_step_loop(K, args.warmup)
     dc_pairs_us = bench.time_pairs(K)
+    # each kernel alone, back to back (the same steady state as the library
+    # ceilings it is compared with)
+    disp_b2b_us = bench.time_loop(bench.dispatch, K)
+    comb_b2b_us = bench.time_loop(bench.combine, K)
     t = bench.time_steps(K, 2)
     st = stats_of(bench, t)
     b = bench.bytes
@@ -793,8 +814,15 @@ def main():
                          "between every call; each event adds ~3 us of its own",
         "cache_flushed": flushed,
         **ceil,
-        "dispatch_frac_of_scatter_ceiling": (round(st["dispatch_GBps"] / ceil["scatter_ceiling_GBps"], 3)
+        "dispatch_back_to_back_us": round(disp_b2b_us, 2),
+        "dispatch_back_to_back_GBps": round(b["dispatch"] / (disp_b2b_us * 1e-6) / 1e9, 1),
+        "combine_back_to_back_us": round(comb_b2b_us, 2),
+        "combine_back_to_back_GBps": round(b["combine"] / (comb_b2b_us * 1e-6) / 1e9, 1),
+        "dispatch_frac_of_scatter_ceiling": (round(b["dispatch"] / (disp_b2b_us * 1e-6) / 1e9
+                                                   / ceil["scatter_ceiling_GBps"], 3)
                                              if "scatter_ceiling_GBps" in ceil else None),
+        "combine_frac_of_gather_ceiling": round(b["combine"] / (comb_b2b_us * 1e-6) / 1e9
+                                                / ceil["gather_ceiling_GBps"], 3),
         "graph_step_us": graph_us,
         "fused_graph_step_us": fused_graph_us,
         "extras": extras,
