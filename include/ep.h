@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 1u
+#define EP_ABI_VERSION 2u  /* 2: row buffers must be 16-byte aligned; ep_layout_noalloc */
 
 /* Limits of this build. */
 #define EP_MAX_RANKS 64    /* R: per-rank buffer pointers travel as kernel arguments */
