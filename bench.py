@@ -461,7 +461,7 @@ def stats_of(bench, t):
         "dispatch_GBps": round(b["dispatch"] / (med["dispatch"] * 1e-6) / 1e9, 1),
         "combine_GBps": round(b["combine"] / (med["combine"] * 1e-6) / 1e9, 1),
         "dc_GBps": round(dc_bytes / (med["dc"] * 1e-6) / 1e9, 1),
-        "dc_frac_of_peak": round(dc_bytes / (med["dc"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "dc_events_frac_of_peak": round(dc_bytes / (med["dc"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
     }
 
 
@@ -623,6 +623,7 @@ def main():
     achieved = b["combine"] / (mean_com * 1e-6) / 1e9
     dc_bytes = b["dispatch"] + b["combine"]
     value = dc_bytes / (dc_pairs_us * 1e-6) / 1e9
+    traffic = load_traffic("combine", args.config)
 
     def pct(v, q):
         s_ = sorted(v)
@@ -778,7 +779,9 @@ def main():
         configs = {}
         for name in CONFIGS:
             if name != args.config:
-                configs[name] = config_summary(name, max(20, min(K, 50)), args.warmup)
+                # 1000 timed iterations for the latency-bound workloads, 100 for the others
+                small = CONFIGS[name]["T"] * CONFIGS[name]["H"] <= 128 * 7168
+                configs[name] = config_summary(name, 1000 if small else 100, args.warmup)
 
     res = {
         "metric": METRIC,
@@ -803,7 +806,8 @@ def main():
                    "combine": "bf16 (fp32 accumulate)", "parallelism": "1 GPU, ranks simulated"},
         "roofline": {"bound": "hbm", "kernel": "combine", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": load_traffic("combine", args.config),
+                     "traffic": traffic,
+                     "traffic_over_algorithmic": (round(traffic / b["combine"], 4) if traffic else None),
                      "algorithmic_bytes_per_launch": b["combine"], "mean_launch_us": round(mean_com, 2),
                      "launch_timing": "HIP events around K back-to-back combine launches on the stream",
                      "event_bracketed_us": round(statistics.mean(t["combine"]), 2)},
@@ -811,6 +815,8 @@ def main():
         "dc_us_p10_p90": [pct(t["dc"], 0.1), pct(t["dc"], 0.9)],
         "dc_back_to_back_us": round(dc_pairs_us, 2),
         "dc_back_to_back_GBps": round(dc_bytes / (dc_pairs_us * 1e-6) / 1e9, 1),
+        "dc_frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
+        "dc_frac_of_copy_ceiling": round(value / ceil["copy_ceiling_GBps"], 4),
         "dc_bytes": dc_bytes,
         "step_bytes": step_bytes,
         "step_us": round(step_us, 2),
