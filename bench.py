@@ -624,6 +624,7 @@ def main():
     dc_bytes = b["dispatch"] + b["combine"]
     value = dc_bytes / (dc_pairs_us * 1e-6) / 1e9
     traffic = load_traffic("combine", args.config)
+    dispatch_traffic = load_traffic("dispatch", args.config)
 
     def pct(v, q):
         s_ = sorted(v)
@@ -825,6 +826,9 @@ def main():
                          "between every call; each event adds ~3 us of its own",
         "cache_flushed": flushed,
         **ceil,
+        "dispatch_traffic": dispatch_traffic,
+        "dispatch_traffic_over_algorithmic": (round(dispatch_traffic / b["dispatch"], 4)
+                                              if dispatch_traffic else None),
         "dispatch_back_to_back_us": round(disp_b2b_us, 2),
         "dispatch_back_to_back_GBps": round(b["dispatch"] / (disp_b2b_us * 1e-6) / 1e9, 1),
         "combine_back_to_back_us": round(comb_b2b_us, 2),
