@@ -567,8 +567,8 @@ def main():
                     help="skip timing the other entry points (router, decode-style, backward, expert-side)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads' lines (the configs block)")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the step captured in a HIP graph and replayed")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step captured in a HIP graph and replayed")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV directories and exit")
     ap.add_argument("--command-prefix", default="", help="recorded in the summary (e.g. env settings)")
@@ -764,7 +764,7 @@ def main():
         bench.check_ok()
 
     graph_us = fused_graph_us = None
-    if args.graph:
+    if not args.no_graph:
         graph_us = round(bench.time_graph([bench.layout, bench.dispatch, bench.combine], K, args.warmup), 2)
         fused_graph_us = round(bench.time_graph([bench.layout_dispatch, bench.combine], K, args.warmup), 2)
 
