@@ -530,11 +530,14 @@ def library_ceilings(bench, reps=8):
     return out
 
 
+GRAPH_STEPS = 10  # steps captured together in one graph for the amortized replay figure
+
+
 def config_summary(name, K, warmup):
     """One line of the configs block: per-call medians and GB/s for layout,
     dispatch and combine on workload `name`, cold-cache medians, and the step
-    replayed from a HIP graph (layout + dispatch + combine, and the one-call
-    layout + dispatch + combine)."""
+    replayed from a HIP graph (layout + dispatch + combine, the one-call
+    layout + dispatch + combine, and ten steps captured in one graph)."""
     b = Bench(name)
     try:
         step_us, _ = b.time_step_loop(K, warmup)
@@ -550,6 +553,10 @@ def config_summary(name, K, warmup):
                "cache_flushed": b.time_cold(min(K, 20))}
         res["graph_step_us"] = round(b.time_graph([b.layout, b.dispatch, b.combine], K, warmup), 2)
         res["graph_fused_step_us"] = round(b.time_graph([b.layout_dispatch, b.combine], K, warmup), 2)
+        # GRAPH_STEPS steps in one graph: the per-launch cost of a replay is
+        # shared by them, as when a whole model step is one graph
+        res["graph_%d_steps_us_per_step" % GRAPH_STEPS] = round(
+            b.time_graph([b.layout, b.dispatch, b.combine] * GRAPH_STEPS, K, warmup) / GRAPH_STEPS, 2)
         return res
     finally:
         b.free()
