@@ -39,7 +39,9 @@
  *   - Pointers are DEVICE pointers unless marked (host).  All memory belongs
  *     to the caller; the library allocates nothing, keeps no pointer after a
  *     call returns and has no global mutable state, so calls on distinct
- *     handles and streams are independent.
+ *     handles and streams are independent.  The one exception is
+ *     ep_layout_noalloc, whose chunk table is a static device array shared
+ *     by all its calls on one GPU (see there).
  *   - Work is enqueued on `stream` and never synchronizes; inputs must stay
  *     alive and unmodified until the stream has passed the call.  Every call
  *     can be captured into a hipGraph (no host sync, no allocation, no memset
