@@ -533,6 +533,17 @@ def library_ceilings(bench, reps=8):
 GRAPH_STEPS = 10  # steps captured together in one graph for the amortized replay figure
 
 
+def guarded(what, fn):
+    """fn() for a secondary figure of the line (extras, configs, graph
+    replays, the CPU baseline): an exception there is reported on stderr and
+    in the line as {"error": ...} instead of costing the headline."""
+    try:
+        return fn()
+    except Exception as e:  # noqa: BLE001 -- any failure of a secondary figure
+        print("bench: %s failed: %r" % (what, e), file=sys.stderr)
+        return {"error": repr(e)[:300]}
+
+
 def config_summary(name, K, warmup):
     """One line of the configs block: per-call medians and GB/s for layout,
     dispatch and combine on workload `name`, cold-cache medians, and the step
@@ -639,8 +650,7 @@ def main():
 
     flushed = bench.time_cold(min(K, 20))
 
-    extras = None
-    if not args.no_extras:
+    def measure_extras():
         # the other entry points on the same handle and buffers: combine with a
         # shared-expert row, and the backward of combine (gradient rows + grad_w)
         gen = bench.gen
@@ -769,17 +779,22 @@ def main():
         extras["routed_fused_step_us"] = round(step_time([rcall, rld, rc]), 2)
         assert int(h2.error_flag.item()) == 0
         bench.check_ok()
+        return extras
+
+    extras = None if args.no_extras else guarded("extras", measure_extras)
 
     graph_us = fused_graph_us = None
     if not args.no_graph:
-        graph_us = round(bench.time_graph([bench.layout, bench.dispatch, bench.combine], K, args.warmup), 2)
-        fused_graph_us = round(bench.time_graph([bench.layout_dispatch, bench.combine], K, args.warmup), 2)
+        graph_us = guarded("graph_step_us", lambda: round(
+            bench.time_graph([bench.layout, bench.dispatch, bench.combine], K, args.warmup), 2))
+        fused_graph_us = guarded("fused_graph_step_us", lambda: round(
+            bench.time_graph([bench.layout_dispatch, bench.combine], K, args.warmup), 2))
 
-    cpu = None
-    if not args.skip_cpu:
+    def measure_cpu():
         yh = [bench.ybufs[r][:bench.rank_counts[r]].cpu().numpy().view(np.uint16) for r in range(w.R)]
-        cpu = cpu_baseline(w, yh)
-        del yh
+        return cpu_baseline(w, yh)
+
+    cpu = None if args.skip_cpu else guarded("cpu_baseline", measure_cpu)
 
     configs = None
     if not args.no_configs:
@@ -789,7 +804,8 @@ def main():
             if name != args.config:
                 # 1000 timed iterations for the latency-bound workloads, 100 for the others
                 small = CONFIGS[name]["T"] * CONFIGS[name]["H"] <= 128 * 7168
-                configs[name] = config_summary(name, 1000 if small else 100, args.warmup)
+                configs[name] = guarded("configs." + name, lambda: config_summary(
+                    name, 1000 if small else 100, args.warmup))
 
     res = {
         "metric": METRIC,

@@ -1,6 +1,7 @@
 """Host-side checks of bench.py: its algorithmic byte model (the bytes the
-method must move per call, which every GB/s figure divides by) and its
-one-GPU guard.  No GPU is used.
+method must move per call, which every GB/s figure divides by), its
+one-GPU guard and its handling of a failing secondary figure.  No GPU is
+used.
 
 The byte model counts, per token, the reads of x and the indices and the
 writes of the k rows (and, for FP8, their per-128-channel scales) for
@@ -62,3 +63,14 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_a_failing_secondary_figure_does_not_cost_the_line(capsys):
+    assert bench.guarded("ok", lambda: {"us": 1.0}) == {"us": 1.0}
+
+    def boom():
+        raise RuntimeError("no such kernel")
+
+    got = bench.guarded("configs.tiny", boom)
+    assert set(got) == {"error"} and "no such kernel" in got["error"]
+    assert "configs.tiny failed" in capsys.readouterr().err
