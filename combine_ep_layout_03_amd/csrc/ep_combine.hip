@@ -14,9 +14,10 @@
 // 128 16-byte chunks (1024 channels) of the output row; one single-wave
 // workgroup takes one unit at a time (grid-stride), so a token's row is spread
 // over several short-lived waves.  Lanes 0..k-1 resolve the token's k received
-// rows and weights; each lane then owns two chunks (c and c+64) and issues the
-// 2*k gathered 16-byte non-temporal loads of its chunks (up to 16 in flight)
-// before any arithmetic, folds them in ascending j with fp32 fused
+// rows (row_addr, from the per-lane rank tables, all of a unit's small loads
+// in one round trip) and weights; each lane then owns two chunks (c and c+64)
+// and issues the 2*k gathered 16-byte non-temporal loads of its chunks (up to
+// 16 in flight) before any arithmetic, folds them in ascending j with fp32 fused
 // multiply-adds from +0, rounds to bf16 nearest-even and writes each output
 // chunk once with a non-temporal store.  No atomics; the un-permute is fused
 // into the loads.  (Measured on MI355X at T=8192, H=7168, k=8: one-wave
@@ -84,34 +85,54 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ slot_of,
     const int32_t *__restrict__ rank_offsets, int32_t *__restrict__ err,
     const float *__restrict__ w, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El,
-    int64_t cap, RankCPtrs ry, const uint16_t *__restrict__ shared, uint16_t *__restrict__ out) {
-  if (*err != 0) return;
+    int32_t R, int64_t cap, RankCPtrs ry, const uint16_t *__restrict__ shared,
+    uint16_t *__restrict__ out) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int nch = H / 8;
   const int nseg = (nch + kSegChunks - 1) / kSegChunks;
   const int64_t units = (int64_t)T * nseg;
-  for (int64_t u = (int64_t)blockIdx.x * kRowWaves + wave; u < units;
-       u += (int64_t)gridDim.x * kRowWaves) {
+  const int64_t u0 = (int64_t)blockIdx.x * kRowWaves + wave;
+  if (u0 >= units) return;
+  int32_t err0 = 0;
+  // One unit; false once the error word is found set (nothing is written).
+  // The token's indices, slots and weights, the per-lane rank tables and the
+  // shared row are loaded together (the error word, read once by the first
+  // unit, after them); the k source rows then come from row_addr's shuffles.
+  auto unit = [&](int64_t u, bool first) -> bool {
     const int64_t t = u / nseg;
     const int c0 = (int)(u % nseg) * kSegChunks + lane;
     const int c1 = c0 + kWave;
     const bool ok0 = c0 < nch, ok1 = c1 < nch;
-    uint64_t src = 0;
+    int32_t e = -1, sl = 0;
     float wj = 0.0f;
     if (lane < k) {
-      src = src_row(idx, slot_of, rank_offsets, err, t * k + lane, E, El, cap, ry, (int64_t)H * 2);
+      e = idx[t * k + lane];
+      sl = slot_of[t * k + lane];
       wj = w ? w[t * k + lane] : 1.0f;
     }
-    if (__ballot(lane < k && src == 0) != 0) continue;  // a bad row: write nothing for t
-    float acc0[8], acc1[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc0[i] = acc1[i] = 0.0f;
+    int32_t my_roff = 0;
+    uint64_t my_base = 0;
+    if (lane < R) {
+      my_roff = rank_offsets[lane];
+      my_base = (uint64_t)ry.p[lane];
+    }
     u32x4 sh0 = {0u, 0u, 0u, 0u}, sh1 = {0u, 0u, 0u, 0u};
     if (HasShared) {
       const u32x4 *srow = reinterpret_cast<const u32x4 *>(shared + t * H);
       if (ok0) sh0 = __builtin_nontemporal_load(srow + c0);
       if (ok1) sh1 = __builtin_nontemporal_load(srow + c1);
     }
+    if (first) err0 = *err;
+    if (err0 != 0) return false;
+    int rank;
+    int64_t row;
+    uint64_t src = row_addr(e, sl, E, El, cap, my_roff, my_base, (int64_t)H * 2, rank, row);
+    if (lane >= k) src = 0;
+    else if (src == 0) atomicOr(err, (int32_t)EP_DEVERR_ROW);
+    if (__ballot(lane < k && src == 0) != 0) return true;  // a bad row: write nothing for t
+    float acc0[8], acc1[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc0[i] = acc1[i] = 0.0f;
     for (int j0 = 0; j0 < k; j0 += kJB) {
       u32x4 v0[kJB], v1[kJB];
 #pragma unroll
@@ -138,7 +159,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     u32x4 *orow = reinterpret_cast<u32x4 *>(out + t * H);
     if (ok0) __builtin_nontemporal_store(pack8(acc0), orow + c0);
     if (ok1) __builtin_nontemporal_store(pack8(acc1), orow + c1);
-  }
+    return true;
+  };
+  // the first unit outside the loop, so that its loads and the error word's
+  // are in flight together (one unit per wave by default)
+  if (!unit(u0, true)) return;
+  for (int64_t u = u0 + (int64_t)gridDim.x * kRowWaves; u < units;
+       u += (int64_t)gridDim.x * kRowWaves)
+    unit(u, false);
 }
 
 // Backward of combine ([DeepEP overview], "Pola penggunaan ...": the backward
@@ -249,32 +277,42 @@ __global__ __launch_bounds__(kBwdThreads) void combine_backward_wg_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ slot_of,
     const int32_t *__restrict__ rank_offsets, int32_t *__restrict__ err,
     const uint16_t *__restrict__ gout, const float *__restrict__ w, int32_t T, int32_t H,
-    int32_t k, int32_t E, int32_t El, int64_t cap, RankCPtrs ry, RankPtrs rg,
+    int32_t k, int32_t E, int32_t El, int32_t R, int64_t cap, RankCPtrs ry, RankPtrs rg,
     float *__restrict__ gw) {
   __shared__ float part[kBwdWaves][EP_MAX_TOPK];  // per-wave dot products
   if (*err != 0) return;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int nch = H / 8;
   const bool want_w = gw != nullptr;
+  // per-lane rank tables (row_addr): the token's rows cost one round trip of
+  // loads instead of a dependent chain, which matters at decode sizes; the
+  // one-wave kernel for large batches keeps the chain (the tables would cost
+  // it a wave per SIMD of occupancy and its long rows hide the chain)
+  int32_t my_roff = 0;
+  uint64_t my_g = 0, my_y = 0;
+  if (lane < R) {
+    my_roff = rank_offsets[lane];
+    my_g = (uint64_t)rg.p[lane];
+    if (want_w) my_y = (uint64_t)ry.p[lane];
+  }
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
     // every wave resolves the token's rows itself (L2 hits), so all waves
     // agree on skipping a bad token without a barrier
-    uint64_t dst = 0, src = 0;
+    int32_t e = -1, sl = 0;
     float wj = 0.0f;
     if (lane < k) {
-      const int64_t p = t * k + lane;
-      const int32_t e = idx[p];
-      if ((uint32_t)e < (uint32_t)E) {
-        const int32_t r = e / El;
-        const int64_t rr = (int64_t)slot_of[p] - rank_offsets[r];
-        if (rr >= 0 && rr < cap) {
-          dst = (uint64_t)rg.p[r] + (uint64_t)(rr * (int64_t)H * 2);
-          if (want_w) src = (uint64_t)ry.p[r] + (uint64_t)(rr * (int64_t)H * 2);
-        }
-      }
-      if (dst == 0 && wave == 0) atomicOr(err, (int32_t)EP_DEVERR_ROW);
-      wj = w ? w[p] : 1.0f;
+      e = idx[t * k + lane];
+      sl = slot_of[t * k + lane];
+      wj = w ? w[t * k + lane] : 1.0f;
     }
+    int rank;
+    int64_t row;
+    uint64_t dst = row_addr(e, sl, E, El, cap, my_roff, my_g, (int64_t)H * 2, rank, row);
+    const uint64_t ybase = shfl64(my_y, rank);
+    uint64_t src = 0;
+    if (lane >= k) dst = 0;
+    else if (dst == 0 && wave == 0) atomicOr(err, (int32_t)EP_DEVERR_ROW);
+    else if (dst != 0 && want_w) src = ybase + (uint64_t)(row * (int64_t)H * 2);
     if (__ballot(lane < k && dst == 0) != 0) continue;  // a bad row: write nothing for t
     const u32x4 *grow = reinterpret_cast<const u32x4 *>(gout + t * H);
     for (int j0 = 0; j0 < k; j0 += kJB) {
@@ -367,13 +405,13 @@ hipError_t launch_combine(const ep_config &c, const ep_layout_t &h, const int32_
   if (shared) {
     hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(kThreads), 0, s, topk_idx, h.slot_of,
                        h.rank_offsets, h.error_flag, w, c.num_tokens, c.hidden, c.num_topk,
-                       c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,
+                       c.num_experts, c.num_experts / c.num_ranks, c.num_ranks, capacity_rows, ry,
                        static_cast<const uint16_t *>(shared), static_cast<uint16_t *>(out));
   } else {
     hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(kThreads), 0, s, topk_idx,
                        h.slot_of, h.rank_offsets, h.error_flag, w, c.num_tokens, c.hidden,
-                       c.num_topk, c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,
-                       nullptr, static_cast<uint16_t *>(out));
+                       c.num_topk, c.num_experts, c.num_experts / c.num_ranks, c.num_ranks,
+                       capacity_rows, ry, nullptr, static_cast<uint16_t *>(out));
   }
   return hipGetLastError();
 }
@@ -388,8 +426,8 @@ hipError_t launch_combine_backward(const ep_config &c, const ep_layout_t &h,
     hipLaunchKernelGGL(combine_backward_wg_kernel, dim3(grid), dim3(kBwdThreads), 0, s, topk_idx,
                        h.slot_of, h.rank_offsets, h.error_flag,
                        static_cast<const uint16_t *>(grad_out), w, c.num_tokens, c.hidden,
-                       c.num_topk, c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,
-                       rg, grad_w);
+                       c.num_topk, c.num_experts, c.num_experts / c.num_ranks, c.num_ranks,
+                       capacity_rows, ry, rg, grad_w);
   } else {
     const int grid = row_grid(c, c.num_tokens);
     hipLaunchKernelGGL(combine_backward_wave_kernel, dim3(grid), dim3(kThreads), 0, s, topk_idx,

@@ -20,6 +20,34 @@ __device__ inline uint64_t readlane64(uint64_t v, int lane) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+__device__ inline uint64_t shfl64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src, kWave);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Address of a pair's row in its rank's buffer, from per-lane rank tables:
+// lane r < R holds rank r's first global slot (my_roff) and buffer base
+// (my_base), loaded once per wave beside its first data loads, so a pair's
+// row costs two shuffles instead of a chain of dependent loads (index, then
+// the rank's offset, then its base pointer).  e and sl are the pair's expert
+// and global slot (lanes without a pair pass e = -1).  Returns 0 when e is
+// outside [0,E) or the row outside [0,cap); rank and row are set either way.
+// Wave-wide: every lane must call it.
+__device__ inline uint64_t row_addr(int32_t e, int32_t sl, int32_t E, int32_t El, int64_t cap,
+                                    int32_t my_roff, uint64_t my_base, int64_t rowbytes,
+                                    int &rank, int64_t &row) {
+  const bool ein = (uint32_t)e < (uint32_t)E;
+  rank = ein ? e / El : 0;
+  const int32_t ro = __shfl(my_roff, rank, kWave);
+  const uint64_t base = shfl64(my_base, rank);
+  // slots and offsets lie in [-1, 2^31): their difference fits 32 bits, and
+  // widening only the difference keeps the compiler from waiting on the slot
+  // load to widen it before the unit's other loads are issued
+  row = (int64_t)(sl - ro);
+  return (ein && row >= 0 && row < cap) ? base + (uint64_t)(row * rowbytes) : 0;
+}
+
 __device__ inline int32_t wave_inclusive_scan(int32_t v, int lane) {
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {

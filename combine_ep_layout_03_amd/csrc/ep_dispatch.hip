@@ -11,9 +11,10 @@
 // Design.  The work unit is one (token, segment) pair and one single-wave
 // workgroup takes one unit at a time (grid-stride), so a token's row is spread
 // over several short-lived waves.  Each unit's slice of the token row is read
-// once and, for FP8, quantized once; lanes 0..k-1 resolve the k destination
-// rows and their base addresses are taken with readlane, so each of the k
-// copies is a scalar-base + vector-offset 16-byte non-temporal store.
+// once and, for FP8, quantized once; lanes 0..k-1 form the k destination rows
+// from the token's indices and slots and the per-lane rank tables (row_addr),
+// and their base addresses are taken with readlane, so each of the k copies is
+// a scalar-base + vector-offset 16-byte non-temporal store.
 //   BF16: a segment is 128 chunks of 16 B (1024 channels), two chunks per lane
 //         (c and c + 64), both loaded before the k copies are stored.
 //   FP8:  a segment is 8 blocks of 128 channels; a lane holds 16 channels
@@ -29,7 +30,10 @@
 // quantization arithmetic, bound this kernel.  Plain stores look faster per
 // call but leave dirty lines in the MALL whose write-back the next kernel
 // pays: slower in steady state.  BF16 at T=4096, H=2048, k=6: two chunks per
-// lane take 1.5 us off one chunk, four add it back.)
+// lane take 1.5 us off one chunk, four add it back.  Issuing every load of a
+// unit at once, instead of resolving index -> rank offset -> base pointer one
+// dependent load at a time, is worth 5 % at decode (T=128) and nothing at
+// T=8192, where the stores bound the kernel.)
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -42,95 +46,114 @@ constexpr int kThreads = kRowWaves * kWave;
 constexpr int kFp8SegBlocks = 8;  // 128-channel blocks per FP8 work unit (= 64 lanes x 16 ch)
 constexpr int kBf16SegChunks = 2 * kWave;  // 16-byte chunks per BF16 work unit (two per lane)
 
-// Lane j < k: byte address of token t's destination row j (0 if unusable,
-// which also raises EP_DEVERR_ROW).  `rowbytes` is the destination row pitch.
-__device__ inline uint64_t dest_row(const int32_t *__restrict__ idx,
-                                    const int32_t *__restrict__ slot_of,
-                                    const int32_t *__restrict__ rank_offsets,
-                                    int32_t *__restrict__ err, int64_t p, int32_t E, int32_t El,
-                                    int64_t cap, const void *const *base, int64_t rowbytes,
-                                    int32_t &rank, int64_t &row) {
-  const int32_t e = idx[p];
-  if ((uint32_t)e < (uint32_t)E) {
-    const int32_t r = e / El;
-    const int64_t rr = (int64_t)slot_of[p] - rank_offsets[r];
-    if (rr >= 0 && rr < cap) {
-      rank = r;
-      row = rr;
-      return (uint64_t)base[r] + (uint64_t)(rr * rowbytes);
-    }
-  }
-  atomicOr(err, (int32_t)EP_DEVERR_ROW);
-  return 0;
-}
-
+// The loads of a unit do not wait for one another: the error word (read once
+// per wave, checked before the first write), the per-lane rank tables, the
+// unit's slice of x and the token's k indices and slots are all in flight
+// together; the destination rows then come from row_addr's shuffles.  A row outside the capacity (a stale handle) raises
+// EP_DEVERR_ROW and the token is skipped.
 __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ slot_of, const int32_t *__restrict__ rank_offsets,
-    int32_t *__restrict__ err, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El, int64_t cap,
-    RankPtrs rx) {
-  if (*err != 0) return;
+    int32_t *__restrict__ err, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El, int32_t R,
+    int64_t cap, RankPtrs rx) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int nch = H / 8;  // 16-byte chunks per row
   const int nseg = (nch + kBf16SegChunks - 1) / kBf16SegChunks;
   const int64_t units = (int64_t)T * nseg;
-  for (int64_t u = (int64_t)blockIdx.x * kRowWaves + wave; u < units;
-       u += (int64_t)gridDim.x * kRowWaves) {
+  const int64_t u0 = (int64_t)blockIdx.x * kRowWaves + wave;
+  if (u0 >= units) return;
+  int32_t err0 = 0;
+  // One unit; false once the error word is found set (nothing is written).
+  // The word is read once, by the first unit, after its other loads are out.
+  auto unit = [&](int64_t u, bool first) -> bool {
     const int64_t t = u / nseg;
     const int c0 = (int)(u % nseg) * kBf16SegChunks + lane;
     const int c1 = c0 + kWave;
-    uint64_t dst = 0;
-    if (lane < k) {
-      int32_t r;
-      int64_t row;
-      dst = dest_row(idx, slot_of, rank_offsets, err, t * k + lane, E, El, cap,
-                     (const void *const *)rx.p, (int64_t)H * 2, r, row);
-    }
-    if (__ballot(lane < k && dst == 0) != 0) continue;  // a bad row: write nothing for t
     const bool ok0 = c0 < nch, ok1 = c1 < nch;
+    int32_t e = -1, sl = 0;
+    if (lane < k) {
+      e = idx[t * k + lane];
+      sl = slot_of[t * k + lane];
+    }
+    int32_t my_roff = 0;
+    uint64_t my_base = 0;
+    if (lane < R) {
+      my_roff = rank_offsets[lane];
+      my_base = (uint64_t)rx.p[lane];
+    }
     const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + t * H);
     u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
     if (ok0) v0 = __builtin_nontemporal_load(xrow + c0);
     if (ok1) v1 = __builtin_nontemporal_load(xrow + c1);
+    if (first) err0 = *err;
+    if (err0 != 0) return false;
+    int rank;
+    int64_t row;
+    uint64_t dst = row_addr(e, sl, E, El, cap, my_roff, my_base, (int64_t)H * 2, rank, row);
+    if (lane >= k) dst = 0;
+    else if (dst == 0) atomicOr(err, (int32_t)EP_DEVERR_ROW);
+    if (__ballot(lane < k && dst == 0) != 0) return true;  // a bad row: write nothing for t
     for (int j = 0; j < k; ++j) {
       u32x4 *d = reinterpret_cast<u32x4 *>(readlane64(dst, j));
       if (ok0) __builtin_nontemporal_store(v0, d + c0);
       if (ok1) __builtin_nontemporal_store(v1, d + c1);
     }
-  }
+    return true;
+  };
+  // the first unit outside the loop, so that its loads and the error word's
+  // are in flight together (one unit per wave by default)
+  if (!unit(u0, true)) return;
+  for (int64_t u = u0 + (int64_t)gridDim.x * kRowWaves; u < units;
+       u += (int64_t)gridDim.x * kRowWaves)
+    unit(u, false);
 }
 
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ slot_of, const int32_t *__restrict__ rank_offsets,
-    int32_t *__restrict__ err, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El, int64_t cap,
-    RankPtrs rq, ScalePtrs rs) {
-  if (*err != 0) return;
+    int32_t *__restrict__ err, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El, int32_t R,
+    int64_t cap, RankPtrs rq, ScalePtrs rs) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int nb = H / 128;  // 128-channel blocks per row
   const int nseg = (nb + kFp8SegBlocks - 1) / kFp8SegBlocks;
   const int64_t units = (int64_t)T * nseg;
-  for (int64_t u = (int64_t)blockIdx.x * kRowWaves + wave; u < units;
-       u += (int64_t)gridDim.x * kRowWaves) {
+  const int64_t u0 = (int64_t)blockIdx.x * kRowWaves + wave;
+  if (u0 >= units) return;
+  int32_t err0 = 0;
+  auto unit = [&](int64_t u, bool first) -> bool {  // as in the BF16 kernel
     const int64_t t = u / nseg;
     const int blk = (int)(u % nseg) * kFp8SegBlocks + lane / 8;
-    uint64_t qdst = 0, sdst = 0;
-    if (lane < k) {
-      int32_t r = 0;
-      int64_t row = 0;
-      qdst = dest_row(idx, slot_of, rank_offsets, err, t * k + lane, E, El, cap,
-                      (const void *const *)rq.p, (int64_t)H, r, row);
-      if (qdst) sdst = (uint64_t)(rs.p[r] + row * nb);
-    }
-    if (__ballot(lane < k && qdst == 0) != 0) continue;  // a bad row: write nothing for t
     const bool valid = blk < nb;
     const int ch = blk * 128 + (lane % 8) * 16;
+    int32_t e = -1, sl = 0;
+    if (lane < k) {
+      e = idx[t * k + lane];
+      sl = slot_of[t * k + lane];
+    }
+    int32_t my_roff = 0;
+    uint64_t my_q = 0, my_s = 0;
+    if (lane < R) {
+      my_roff = rank_offsets[lane];
+      my_q = (uint64_t)rq.p[lane];
+      my_s = (uint64_t)rs.p[lane];
+    }
     const uint16_t *xrow = x + t * H;
     u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
     if (valid) {
       v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch));
       v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch + 8));
     }
+    if (first) err0 = *err;
+    if (err0 != 0) return false;
+    int rank;
+    int64_t row;
+    uint64_t qdst = row_addr(e, sl, E, El, cap, my_roff, my_q, (int64_t)H, rank, row);
+    const uint64_t sbase = shfl64(my_s, rank);
+    uint64_t sdst = 0;
+    if (lane >= k) qdst = 0;
+    else if (qdst == 0) atomicOr(err, (int32_t)EP_DEVERR_ROW);
+    else sdst = sbase + (uint64_t)(row * nb * 4);
+    if (__ballot(lane < k && qdst == 0) != 0) return true;  // a bad row: write nothing for t
     // 8 lanes per block: invalid lanes form whole groups of 8 and stay at 0
     float s;
     const u32x4 q = quant_block16(v0, v1, s);
@@ -142,7 +165,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
         if ((lane % 8) == 0) sd[blk] = s;
       }
     }
-  }
+    return true;
+  };
+  if (!unit(u0, true)) return;
+  for (int64_t u = u0 + (int64_t)gridDim.x * kRowWaves; u < units;
+       u += (int64_t)gridDim.x * kRowWaves)
+    unit(u, false);
 }
 
 }  // namespace
@@ -157,14 +185,14 @@ hipError_t launch_dispatch(const ep_config &c, const ep_layout_t &h, const int32
     hipLaunchKernelGGL(dispatch_fp8_kernel, dim3(grid), dim3(kThreads), 0, s,
                        static_cast<const uint16_t *>(x), topk_idx, h.slot_of, h.rank_offsets,
                        h.error_flag, c.num_tokens, c.hidden, c.num_topk, c.num_experts, El,
-                       capacity_rows, rx, rs);
+                       c.num_ranks, capacity_rows, rx, rs);
   } else {
     const int64_t nseg = (c.hidden / 8 + kBf16SegChunks - 1) / kBf16SegChunks;
     const int grid = row_grid(c, (int64_t)c.num_tokens * nseg);
     hipLaunchKernelGGL(dispatch_bf16_kernel, dim3(grid), dim3(kThreads), 0, s,
                        static_cast<const uint16_t *>(x), topk_idx, h.slot_of, h.rank_offsets,
                        h.error_flag, c.num_tokens, c.hidden, c.num_topk, c.num_experts, El,
-                       capacity_rows, rx);
+                       c.num_ranks, capacity_rows, rx);
   }
   return hipGetLastError();
 }

@@ -69,14 +69,20 @@ __global__ __launch_bounds__(kWave) void layout_dispatch_small_kernel(
   const int nseg = FP8 ? (nb + kFp8SegBlocks - 1) / kFp8SegBlocks : (nch + kWave - 1) / kWave;
   const int64_t units = (int64_t)T * nseg;
 
-  // the first unit's payload and its token's k indices, loaded now so that
-  // they overlap the layout work
+  // the first unit's payload and its token's k indices, and the ranks'
+  // buffer bases (lane r < R holds rank r's, taken later with a shuffle),
+  // loaded now so that they overlap the layout work
   int64_t u = blockIdx.x;
   u32x4 pv0, pv1;
   int32_t e_first = 0;
   if (u < units) {
     load_payload<FP8>(x, u / nseg, (int)(u % nseg), H, lane, pv0, pv1);
     if (lane < k) e_first = idx[(u / nseg) * k + lane];
+  }
+  uint64_t my_q = 0, my_s = 0;
+  if (lane < R) {
+    my_q = (uint64_t)rq.p[lane];
+    if (FP8) my_s = (uint64_t)rs.p[lane];
   }
 
   // every index, coalesced: value i of this lane is pair i*64 + lane
@@ -163,12 +169,14 @@ __global__ __launch_bounds__(kWave) void layout_dispatch_small_kernel(
     }
     for (int j = 0; j < k; ++j) my_slot += (j < lane && (int32_t)rdl((uint32_t)my_e, j) == my_e) ? 1 : 0;
     uint64_t dst = 0, sdst = 0;
+    const int32_t r = (lane < k) ? my_e / El : 0;
+    const uint64_t qbase = shfl64(my_q, r);
+    const uint64_t sbase = FP8 ? shfl64(my_s, r) : 0;
     if (lane < k) {
-      const int32_t r = my_e / El;
       const int64_t row = (int64_t)my_slot - off[r * El];
       if (row >= 0 && row < cap) {  // always holds: slots are < T*k <= cap
-        dst = (uint64_t)rq.p[r] + (uint64_t)(row * (FP8 ? (int64_t)H : (int64_t)H * 2));
-        if (FP8) sdst = (uint64_t)(rs.p[r] + row * nb);
+        dst = qbase + (uint64_t)(row * (FP8 ? (int64_t)H : (int64_t)H * 2));
+        if (FP8) sdst = sbase + (uint64_t)(row * nb * 4);
       }
       if (seg == 0) {
         const int64_t p = t * k + lane;
