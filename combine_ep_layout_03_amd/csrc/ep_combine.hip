@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
       if (ok1) sh1 = __builtin_nontemporal_load(srow + c1);
     }
     if (first) err0 = *err;
-    if (err0 != 0) return false;
+    if (err0 & kLayoutErrBits) return false;
     int rank;
     int64_t row;
     uint64_t src = row_addr(e, sl, E, El, cap, my_roff, my_base, (int64_t)H * 2, rank, row);
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void combine_backward_wave_kernel(
     const uint16_t *__restrict__ gout, const float *__restrict__ w, int32_t T, int32_t H,
     int32_t k, int32_t E, int32_t El, int64_t cap, RankCPtrs ry, RankPtrs rg,
     float *__restrict__ gw) {
-  if (*err != 0) return;
+  if (*err & kLayoutErrBits) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int nch = H / 8;
   const bool want_w = gw != nullptr;
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kBwdThreads) void combine_backward_wg_kernel(
     int32_t k, int32_t E, int32_t El, int32_t R, int64_t cap, RankCPtrs ry, RankPtrs rg,
     float *__restrict__ gw) {
   __shared__ float part[kBwdWaves][EP_MAX_TOPK];  // per-wave dot products
-  if (*err != 0) return;
+  if (*err & kLayoutErrBits) return;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int nch = H / 8;
   const bool want_w = gw != nullptr;
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ slot_of,
     const int32_t *__restrict__ rank_offsets, int32_t *__restrict__ err, int64_t P, int32_t H,
     int32_t E, int32_t El, int64_t cap, RankCPtrs ry, uint16_t *__restrict__ out) {
-  if (*err != 0) return;
+  if (*err & kLayoutErrBits) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int nch = H / 8;
   for (int64_t p = (int64_t)blockIdx.x * kRowWaves + wave; p < P;

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     if (ok0) v0 = __builtin_nontemporal_load(xrow + c0);
     if (ok1) v1 = __builtin_nontemporal_load(xrow + c1);
     if (first) err0 = *err;
-    if (err0 != 0) return false;
+    if (err0 & kLayoutErrBits) return false;
     int rank;
     int64_t row;
     uint64_t dst = row_addr(e, sl, E, El, cap, my_roff, my_base, (int64_t)H * 2, rank, row);
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
       v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + ch + 8));
     }
     if (first) err0 = *err;
-    if (err0 != 0) return false;
+    if (err0 & kLayoutErrBits) return false;
     int rank;
     int64_t row;
     uint64_t qdst = row_addr(e, sl, E, El, cap, my_roff, my_q, (int64_t)H, rank, row);

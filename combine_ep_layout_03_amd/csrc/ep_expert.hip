@@ -55,7 +55,7 @@ __device__ inline float exp_neg(float g) {
 __global__ __launch_bounds__(kWave) void silu_mul_quant_kernel(
     const int32_t *__restrict__ rank_offsets, const int32_t *__restrict__ err, int64_t P,
     int32_t R, int32_t I, int64_t cap, RankCPtrs in, RankPtrs q_out, ScalePtrs s_out) {
-  if (*err != 0) return;
+  if (*err & kLayoutErrBits) return;
   const int lane = threadIdx.x;
   const int nb = I / 128;
   const int nseg = (nb + kSegBlocks - 1) / kSegBlocks;

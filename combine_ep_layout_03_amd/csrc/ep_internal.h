@@ -40,6 +40,11 @@ constexpr int kLayoutWaves = 4;  // wavefronts per layout workgroup
 constexpr int kLayoutMaxChunks = kLayoutWaves * kWave;  // C <= threads of a layout workgroup
 constexpr int kLayoutChunk = 512;  // pairs per chunk (= per wavefront) of the two-launch layout
 constexpr int kRowWaves = 1;     // wavefronts per dispatch / combine workgroup
+// Error-word bits that make a call write nothing: the layout's own findings
+// (set before any call that reads the handle).  EP_DEVERR_ROW is checked per
+// pair instead, so a row error found by one wave of a call does not change
+// what the call's other waves write.
+constexpr int32_t kLayoutErrBits = EP_DEVERR_INDEX | EP_DEVERR_INTERNAL;
 constexpr int kSmallWaves = 16;  // wavefronts of the single-workgroup layout
 constexpr int64_t kSmallMaxPairs = 8192;    // T*k limit of the single-launch layout
 constexpr int kSmallMaxExperts = 384;       // E limit of the single-launch layout (LDS <= 64 KB)

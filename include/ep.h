@@ -58,10 +58,14 @@
  *     a view that starts inside a row is not.  The index, weight and logit
  *     arrays need only their element alignment.
  *   - Data problems found on the device (a routing index outside [0,E), a
- *     row outside the capacity) set bits in the handle's error word; every
+ *     row outside the capacity) set bits in the handle's error word.  Every
  *     call that reads a handle (dispatch, combine with or without the shared
  *     expert, combine backward, the SiLU re-quantization, unpermute) reads
- *     the word first and then writes nothing.
+ *     the word first and writes nothing when the layout flagged the handle
+ *     (EP_DEVERR_INDEX or EP_DEVERR_INTERNAL).  A row outside the capacity
+ *     (a stale handle) is checked per pair: the pair's token is skipped and
+ *     EP_DEVERR_ROW set, and every other token is written, so what a call
+ *     writes does not depend on the order its waves run in.
  *   - Output bytes do not depend on ep_config.num_workgroups.
  *
  * Data types: routing indices int32 [T,k] row-major; weights fp32 [T,k];
@@ -103,7 +107,8 @@ typedef int32_t ep_status;
  * one-launch layout has one workgroup write it).  Later calls only OR bits
  * in. */
 #define EP_DEVERR_INDEX 1u    /* ep_layout saw an index outside [0,E) */
-#define EP_DEVERR_ROW 2u      /* dispatch/combine saw a row outside [0,capacity) */
+#define EP_DEVERR_ROW 2u      /* a call saw a row outside [0,capacity) and skipped
+                                 that row's token */
 #define EP_DEVERR_INTERNAL 4u /* ep_layout computed a slot outside [0,T*k): a library
                                  bug.  Such a pair's slot_of is -1, so later calls on
                                  the handle report EP_DEVERR_ROW for its token even

@@ -165,6 +165,52 @@ def test_stale_handle_rows_are_rejected_on_device():
     assert all(np.all(a.view(np.uint8) == POISON) for a in xs)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("nwg", [0, 1, 3])
+def test_partly_stale_handle_skips_only_the_bad_tokens(fp8, nwg):
+    """A handle laid out with every pair on expert 0 (rank 0), then used with
+    indices that move the second half of the tokens to rank R-1: their rows
+    fall outside rank R-1's range and are skipped with EP_DEVERR_ROW, while
+    the first half is dispatched and combined exactly as the oracle does
+    under the original routing.  Only the layout's error bits stop a call, so
+    the row error one wave raises changes nothing another wave writes, nor
+    (num_workgroups 1 or 3: each wave takes many units in turn) what the same
+    wave writes later, nor what a later call writes."""
+    T, H, k, E, R = 64, 256, 2, 8, 4
+    say(f"partly stale handle fp8={fp8} num_workgroups={nwg}")
+    w = custom("stale_half", T, H, k, E, R, fp8, np.zeros((T, k)))
+    run = GpuRun(w, num_workgroups=nwg).layout()
+    L = check_layout(w, run)
+    good = T // 2
+    moved = np.zeros((T, k), np.int32)
+    moved[good:] = E - 1
+    run.idx = to_dev(moved)
+    run.dispatch()
+    g = run.handle_np()
+    assert g["error_flag"][0] == ep.EP_DEVERR_ROW
+    xs, ss = run.recv_np(None, full=True)
+    n = good * k  # the good tokens' pairs hold slots [0, n) of rank 0
+    if fp8:
+        rq, rs = oracle.dispatch_fp8(w.x, w.topk_idx, L)
+        assert np.array_equal(xs[0][:n], rq[0][:n])
+        assert np.array_equal(ss[0][:n].view(np.uint32), rs[0][:n].view(np.uint32))
+        assert np.all(ss[0][n:].view(np.uint8) == POISON)
+    else:
+        assert np.array_equal(xs[0][:n], oracle.dispatch_bf16(w.x, w.topk_idx, L)[0][:n])
+    assert np.all(xs[0][n:].view(np.uint8) == POISON)
+    assert all(np.all(a.view(np.uint8) == POISON) for a in xs[1:])
+    # combine under the moved indices; the word still holds the dispatch's
+    # row error, which does not stop it
+    ys = expert_rows_for(w, L)
+    run.put_expert_rows(ys).combine()
+    torch.cuda.synchronize()
+    assert int(run.h.error_flag[0]) == ep.EP_DEVERR_ROW
+    got = u16(run.out)
+    ref = oracle.combine(ys, w.topk_idx, L, w.topk_w)
+    assert rel_err(got[:good], ref[:good]) <= 1e-2
+    assert np.all(got[good:].view(np.uint8) == POISON)
+
+
 # ---------------------------------------------------------------- dispatch
 def check_dispatch(w, run, L):
     xs, ss = run.recv_np(L.rank_counts, full=True)
