@@ -209,6 +209,29 @@ def test_partly_stale_handle_skips_only_the_bad_tokens(fp8, nwg):
     ref = oracle.combine(ys, w.topk_idx, L, w.topk_w)
     assert rel_err(got[:good], ref[:good]) <= 1e-2
     assert np.all(got[good:].view(np.uint8) == POISON)
+    # un-permute: the good pairs' rows, the others untouched
+    u = u16(run.unpermute())
+    assert np.array_equal(u[:n], oracle.unpermute(ys, w.topk_idx, L)[:n])
+    assert np.all(u[n:].view(np.uint8) == POISON)
+    # combine backward (one-wave or workgroup kernel by T): the good tokens'
+    # gradient rows and weight gradients, nothing for the others
+    rng = np.random.default_rng(3)
+    g = bf16_from_f32(rng.standard_normal((T, H), dtype=np.float32))
+    grows = [torch.full((run.cap, H), -21846, dtype=torch.int16, device="cuda") for _ in range(R)]
+    gw = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+    ep.ep_combine_backward(run.cfg, run.h, run.idx, to_dev(g), run.wts, run.ybufs, grows, gw, run.cap)
+    torch.cuda.synchronize()
+    ref_rows, ref_gw = oracle.combine_backward(g, w.topk_idx, L, w.topk_w, ys)
+    got_rows = grows[0].cpu().numpy().view(np.uint16)
+    assert np.array_equal(got_rows[:n], ref_rows[0][:n])
+    assert np.all(got_rows[n:].view(np.uint8) == POISON)
+    got_gw = gw.cpu().numpy()
+    assert np.all(np.isnan(got_gw[good:]))
+    yrow = oracle.bf16_to_f32(np.concatenate(ys)[L.slot_of]).astype(np.float64).reshape(T, k, H)
+    mag = np.einsum("th,tkh->tk", np.abs(oracle.bf16_to_f32(g).astype(np.float64)), np.abs(yrow))
+    err = np.abs(got_gw[:good].astype(np.float64) - ref_gw[:good].astype(np.float64))
+    assert np.all(err <= 1e-5 * mag[:good] + 1e-30)
+    assert int(run.h.error_flag[0]) == ep.EP_DEVERR_ROW
 
 
 # ---------------------------------------------------------------- dispatch
