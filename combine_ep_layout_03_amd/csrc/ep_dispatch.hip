@@ -32,7 +32,7 @@
 // pays: slower in steady state.  BF16 at T=4096, H=2048, k=6: two chunks per
 // lane take 1.5 us off one chunk, four add it back.  Issuing every load of a
 // unit at once, instead of resolving index -> rank offset -> base pointer one
-// dependent load at a time, is worth 5 % at decode (T=128) and nothing at
+// dependent load at a time, is worth 13 % at decode (T=128) and nothing at
 // T=8192, where the stores bound the kernel.)
 #include "ep_device.h"
 #include "ep_internal.h"
