@@ -11,9 +11,14 @@
 
 namespace {
 
+// EP_DEBUG is read once, at the first call that asks (a getenv per call is a
+// scan of the environment, a measurable share of a small call's host time).
 bool debug_enabled() {
-  const char *v = std::getenv("EP_DEBUG");
-  return v && v[0] && v[0] != '0';
+  static const bool on = [] {
+    const char *v = std::getenv("EP_DEBUG");
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
 }
 
 bool config_ok(const ep_config *c) {
