@@ -159,10 +159,11 @@ def cpu_baseline(w, ybufs_host, reps=3):
 
 
 # rocprofv3 kernel names ("ep::(anonymous namespace)::combine_kernel<false>(int const*, ...")
-# matched by anchored patterns: combine_kernel<false> is ep_combine, <true> ep_combine_shared;
-# route_rows_kernel<N, true> is the router that also counts the layout's chunk table
+# matched by anchored patterns: combine_kernel<false> and combine_chain_kernel<false> (the
+# form large batches take) are ep_combine, <true> ep_combine_shared; route_rows_kernel<N, true>
+# is the router that also counts the layout's chunk table
 KERNEL_KEYS = {
-    "combine": r"::combine_kernel(<false>)?\(",
+    "combine": r"::combine_(chain_)?kernel(<false>)?\(",
     "dispatch": r"::dispatch_(fp8|bf16)_kernel\(",
     "layout_count": r"::layout_count_kernel\(",
     "layout_scatter": r"::layout_scatter_kernel\(",
@@ -171,7 +172,7 @@ KERNEL_KEYS = {
     "route": r"::(route_kernel<\d+>|route_rows_kernel<\d+, false>)\(",
     "route_count": r"::route_rows_kernel<\d+, true>\(",
     "layout_dispatch_small": r"::layout_dispatch_small_kernel<(true|false)>\(",
-    "combine_shared": r"::combine_kernel<true>\(",
+    "combine_shared": r"::combine_(chain_)?kernel<true>\(",
     "combine_backward": r"::combine_backward_(wave|wg)_kernel\(",
     "silu_mul_quant": r"::silu_mul_quant_kernel\(",
 }
