@@ -13,12 +13,14 @@
 // Design.  The work unit is one (token, segment) pair, where a segment is
 // 128 16-byte chunks (1024 channels) of the output row; one single-wave
 // workgroup takes one unit at a time (grid-stride), so a token's row is spread
-// over several short-lived waves.  Lanes 0..k-1 resolve the token's k received
-// rows (row_addr, from the per-lane rank tables, all of a unit's small loads
-// in one round trip) and weights; each lane then owns two chunks (c and c+64)
-// and issues the 2*k gathered 16-byte non-temporal loads of its chunks (up to
-// 16 in flight) before any arithmetic, folds them in ascending j with fp32 fused
-// multiply-adds from +0, rounds to bf16 nearest-even and writes each output
+// over several short-lived waves.  Lanes 0..k-1 resolve the token's k
+// received rows (up to 16384 units from the per-lane rank tables, all of a
+// unit's small loads in one round trip; above, by a chain of dependent loads,
+// which the memory queues hide there) and weights; each lane then owns two
+// chunks (c and c+64) and issues the 2*k gathered 16-byte non-temporal loads
+// of its chunks (up to 16 in flight) before any arithmetic, folds them in
+// ascending j with fp32 fused multiply-adds from +0, rounds to bf16
+// nearest-even and writes each output
 // chunk once with a non-temporal store.  No atomics; the un-permute is fused
 // into the loads.  (Measured on MI355X at T=8192, H=7168, k=8: one-wave
 // workgroups and two chunks per lane beat four-wave workgroups, one chunk and
