@@ -328,13 +328,17 @@ __device__ void wave_walk(const int32_t *__restrict__ idx, int64_t p0, int64_t p
 // (The one-workgroup small path took 8 us at 1024 pairs, a chain of
 // barriers and per-wave prefix loops.)
 constexpr int kTinyPL = (int)(kFusedMaxPairs / kWave);
+static_assert(kFusedMaxPairs < (1 << 16), "the decode layout packs two 16-bit counts per expert");
 
 __global__ __launch_bounds__(kWave) void layout_tiny_kernel(const int32_t *__restrict__ idx,
                                                             int64_t P, int32_t E, int32_t R,
                                                             ep_layout_t h) {
   extern __shared__ int32_t lds[];
-  int32_t *tot = lds;          // [E+1] totals, then exclusive offsets
-  int32_t *pre = lds + E + 1;  // [E]   pairs of e before this workgroup's 64
+  // [E] an expert's two counts in one word, so a pair costs one LDS atomic:
+  // low 16 bits all its pairs, high 16 bits those before this workgroup's 64
+  // (each < 2^16: P <= kFusedMaxPairs)
+  uint32_t *cnt = reinterpret_cast<uint32_t *>(lds);
+  int32_t *tot = lds + E;  // [E+1] exclusive offsets
   const int lane = threadIdx.x;
   const int nv = (int)((P + kWave - 1) / kWave);
   const int64_t p = (int64_t)blockIdx.x * kWave + lane;  // this lane's own pair
@@ -348,15 +352,13 @@ __global__ __launch_bounds__(kWave) void layout_tiny_kernel(const int32_t *__res
     ev[i] = (i < nv && q < P) ? idx[q] : 0;
     if (i < nv && q < P && (uint32_t)ev[i] >= (uint32_t)E) ++bad;
   }
-  for (int e = lane; e < 2 * E + 1; e += kWave) lds[e] = 0;
+  for (int e = lane; e < E; e += kWave) cnt[e] = 0u;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kTinyPL; ++i) {
     const int64_t q = (int64_t)i * kWave + lane;
-    if (i < nv && q < P && (uint32_t)ev[i] < (uint32_t)E) {
-      atomicAdd(&tot[ev[i]], 1);
-      if (i < (int)blockIdx.x) atomicAdd(&pre[ev[i]], 1);  // pair q = 64i + lane precedes 64g
-    }
+    if (i < nv && q < P && (uint32_t)ev[i] < (uint32_t)E)  // pair q = 64i + lane precedes 64g if i < g
+      atomicAdd(&cnt[ev[i]], (i < (int)blockIdx.x) ? 0x10001u : 1u);
   }
   bad = dev::wave_sum_u32(bad);
   __syncthreads();
@@ -365,11 +367,11 @@ __global__ __launch_bounds__(kWave) void layout_tiny_kernel(const int32_t *__res
     const int b = (lane * per < E) ? lane * per : E;
     const int end = (b + per < E) ? b + per : E;
     int32_t s = 0;
-    for (int i = b; i < end; ++i) s += tot[i];
+    for (int i = b; i < end; ++i) s += (int32_t)(cnt[i] & 0xFFFFu);
     const int32_t incl = wave_inclusive_scan(s, lane);
     int32_t run = incl - s;
     for (int i = b; i < end; ++i) {
-      const int32_t v = tot[i];
+      const int32_t v = (int32_t)(cnt[i] & 0xFFFFu);
       tot[i] = run;
       run += v;
     }
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(kWave) void layout_tiny_kernel(const int32_t *__res
   }
   if (own) {
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    const int32_t slot = tot[pe] + pre[pe] + __popcll(m & below);
+    const int32_t slot = tot[pe] + (int32_t)(cnt[pe] >> 16) + __popcll(m & below);
     if ((uint64_t)(uint32_t)slot < (uint64_t)P) {
       h.slot_of[p] = slot;
       h.src_of[slot] = (int32_t)p;
