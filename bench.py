@@ -173,7 +173,9 @@ KERNEL_KEYS = {
     "route_count": r"::route_rows_kernel<\d+, true>\(",
     "layout_dispatch_small": r"::layout_dispatch_small_kernel<(true|false)>\(",
     "combine_shared": r"::combine_(chain_)?kernel<true>\(",
-    "combine_backward": r"::combine_backward_(wave|wg)_kernel\(",
+    "combine_backward_rows": r"::combine_backward_rows_kernel\(",
+    "combine_backward_dots": r"::combine_backward_dots_kernel\(",
+    "combine_backward_wg": r"::combine_backward_wg_kernel\(",
     "silu_mul_quant": r"::silu_mul_quant_kernel\(",
 }
 CAL_COPY_KEY = "bitwise_not"      # elementwise kernel: reads and writes CAL_BYTES

@@ -55,13 +55,6 @@ __device__ inline void add8(float *acc, u32x4 v) {
   }
 }
 
-__device__ inline u32x4 pack8(const float *acc) {
-  u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = bf16_bits(acc[2 * i]) | (bf16_bits(acc[2 * i + 1]) << 16);
-  return o;
-}
-
 // Lane j < k: byte address of pair (t, j)'s received row (0 if unusable,
 // which raises EP_DEVERR_ROW).
 __device__ inline uint64_t src_row(const int32_t *__restrict__ idx,
@@ -89,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     const float *__restrict__ w, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El,
     int32_t R, int64_t cap, RankCPtrs ry, const uint16_t *__restrict__ shared,
     uint16_t *__restrict__ out) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = wave_id(), lane = threadIdx.x % kWave;
   const int nch = H / 8;
   const int nseg = (nch + kSegChunks - 1) / kSegChunks;
   const int64_t units = (int64_t)T * nseg;
@@ -184,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void combine_chain_kernel(
     const float *__restrict__ w, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El,
     int64_t cap, RankCPtrs ry, const uint16_t *__restrict__ shared, uint16_t *__restrict__ out) {
   if (*err & kLayoutErrBits) return;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = wave_id(), lane = threadIdx.x % kWave;
   const int nch = H / 8;
   const int nseg = (nch + kSegChunks - 1) / kSegChunks;
   const int64_t units = (int64_t)T * nseg;
@@ -240,42 +233,41 @@ __global__ __launch_bounds__(kThreads) void combine_chain_kernel(
 }
 
 // Backward of combine ([DeepEP overview], "Pola penggunaan ...": the backward
-// of combine is a dispatch), for large batches.  One wave per token
-// (grid-stride); the k pairs
-// are taken in blocks of 8: for each block the wave streams the token's
-// grad_out row once, writes bf16(RN32(w_j * g)) into each pair's gradient row
-// and, when y is given, accumulates each pair's dot product <g, y_j> per lane
-// (fp32 fma over the lane's channels in order), then reduces it across the
-// wave with a fixed xor-butterfly, so the result is deterministic.
-__global__ __launch_bounds__(kThreads) void combine_backward_wave_kernel(
+// of combine is a dispatch), for large batches, in two launches.  The
+// gradient rows bf16(RN32(w_j * g)) are a BF16 dispatch of grad_out with one
+// multiply per copy (combine_backward_rows_kernel, ep_dispatch.hip, capped
+// like dispatch at 12 resident workgroups per CU); this kernel then computes
+// grad_w alone: one wave per token (grid-stride), the k pairs in blocks of 8,
+// for each block the token's grad_out row streamed once beside the block's
+// received rows, each pair's dot product <g, y_j> accumulated per lane (fp32
+// fma over the lane's channels in order) and reduced across the wave with a
+// fixed xor-butterfly, so the result is deterministic.  A token with an
+// unusable row gets no grad_w (the rows kernel raises EP_DEVERR_ROW for it).
+// (Measured on MI355X at T=8192, H=7168, k=8: 212 + 157 us against 387 us
+// for one wave per token writing the rows and the dots together, whose
+// scattered row stores and gathered row loads shared each wave; 329 against
+// 382 us with Zipf-skewed routing; equal at T=4096, H=2048, k=6.)
+__global__ __launch_bounds__(kThreads) void combine_backward_dots_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ slot_of,
-    const int32_t *__restrict__ rank_offsets, int32_t *__restrict__ err,
-    const uint16_t *__restrict__ gout, const float *__restrict__ w, int32_t T, int32_t H,
-    int32_t k, int32_t E, int32_t El, int64_t cap, RankCPtrs ry, RankPtrs rg,
-    float *__restrict__ gw) {
+    const int32_t *__restrict__ rank_offsets, const int32_t *__restrict__ err,
+    const uint16_t *__restrict__ gout, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El,
+    int64_t cap, RankCPtrs ry, float *__restrict__ gw) {
   if (*err & kLayoutErrBits) return;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = wave_id(), lane = threadIdx.x % kWave;
   const int nch = H / 8;
-  const bool want_w = gw != nullptr;
   for (int64_t t = (int64_t)blockIdx.x * kRowWaves + wave; t < T;
        t += (int64_t)gridDim.x * kRowWaves) {
-    uint64_t dst = 0, src = 0;
-    float wj = 0.0f;
+    uint64_t src = 0;
     if (lane < k) {
       const int64_t p = t * k + lane;
       const int32_t e = idx[p];
       if ((uint32_t)e < (uint32_t)E) {
         const int32_t r = e / El;
         const int64_t rr = (int64_t)slot_of[p] - rank_offsets[r];
-        if (rr >= 0 && rr < cap) {
-          dst = (uint64_t)rg.p[r] + (uint64_t)(rr * (int64_t)H * 2);
-          if (want_w) src = (uint64_t)ry.p[r] + (uint64_t)(rr * (int64_t)H * 2);
-        }
+        if (rr >= 0 && rr < cap) src = (uint64_t)ry.p[r] + (uint64_t)(rr * (int64_t)H * 2);
       }
-      if (dst == 0) atomicOr(err, (int32_t)EP_DEVERR_ROW);
-      wj = w ? w[p] : 1.0f;
     }
-    if (__ballot(lane < k && dst == 0) != 0) continue;  // a bad row: write nothing for t
+    if (__ballot(lane < k && src == 0) != 0) continue;  // a bad row: no grad_w for t
     const u32x4 *grow = reinterpret_cast<const u32x4 *>(gout + t * H);
     for (int j0 = 0; j0 < k; j0 += kJB) {
       float acc[kJB];
@@ -284,61 +276,48 @@ __global__ __launch_bounds__(kThreads) void combine_backward_wave_kernel(
       for (int c = lane; c < nch; c += kWave) {
         const u32x4 g = grow[c];
         u32x4 v[kJB];
-        if (want_w) {
 #pragma unroll
-          for (int jj = 0; jj < kJB; ++jj)
-            if (j0 + jj < k)
-              v[jj] = __builtin_nontemporal_load(
-                  reinterpret_cast<const u32x4 *>(readlane64(src, j0 + jj)) + c);
-        }
+        for (int jj = 0; jj < kJB; ++jj)
+          if (j0 + jj < k)
+            v[jj] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(readlane64(src, j0 + jj)) + c);
 #pragma unroll
         for (int jj = 0; jj < kJB; ++jj) {
           if (j0 + jj < k) {
-            const float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j0 + jj));
-            float prod[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              prod[2 * i] = wv * __uint_as_float(g[i] << 16);
-              prod[2 * i + 1] = wv * __uint_as_float(g[i] & 0xFFFF0000u);
-            }
-            u32x4 *drow = reinterpret_cast<u32x4 *>(readlane64(dst, j0 + jj));
-            __builtin_nontemporal_store(pack8(prod), drow + c);
-            if (want_w) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                acc[jj] = __builtin_fmaf(__uint_as_float(g[i] << 16),
-                                         __uint_as_float(v[jj][i] << 16), acc[jj]);
-                acc[jj] = __builtin_fmaf(__uint_as_float(g[i] & 0xFFFF0000u),
-                                         __uint_as_float(v[jj][i] & 0xFFFF0000u), acc[jj]);
-              }
+              acc[jj] = __builtin_fmaf(__uint_as_float(g[i] << 16),
+                                       __uint_as_float(v[jj][i] << 16), acc[jj]);
+              acc[jj] = __builtin_fmaf(__uint_as_float(g[i] & 0xFFFF0000u),
+                                       __uint_as_float(v[jj][i] & 0xFFFF0000u), acc[jj]);
             }
           }
         }
       }
-      if (want_w) {
 #pragma unroll
-        for (int jj = 0; jj < kJB; ++jj) {
-          float a = acc[jj];
+      for (int jj = 0; jj < kJB; ++jj) {
+        float a = acc[jj];
 #pragma unroll
-          for (int o = kWave / 2; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
-          if (lane == 0 && j0 + jj < k) gw[t * k + j0 + jj] = a;
-        }
+        for (int o = kWave / 2; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+        if (lane == 0 && j0 + jj < k) gw[t * k + j0 + jj] = a;
       }
     }
   }
 }
 
-// The same for small batches (T < kBwdWgMaxTokens, e.g. decode), where one
-// wave per token leaves the GPU nearly idle.  One workgroup of kBwdWaves waves per token
-// (grid-stride), its threads splitting the row's 16-byte chunks; the k pairs
+// The backward for small batches (T < kBwdWgMaxTokens, e.g. decode), in one
+// launch, since there a second launch costs more than it saves and one wave
+// per token leaves the GPU nearly idle.  One workgroup of kBwdWaves waves per
+// token (grid-stride), its threads splitting the row's 16-byte chunks; the k pairs
 // are taken in blocks of 8: for each block the workgroup streams the token's
 // grad_out row once, writes bf16(RN32(w_j * g)) into each pair's gradient row
 // and, when y is given, accumulates each pair's dot product <g, y_j> per
 // thread (fp32 fma over its channels in order), reduces it across each wave
 // with a fixed xor-butterfly and then over the waves in ascending order, so
 // the result is deterministic and needs no scratch memory.  (Measured on
-// MI355X: at 128 tokens 16 us against 50 us for one wave per token; at 8192
-// tokens 411 us against 387 us, hence the split.)
+// MI355X: at 128 tokens 16 us against 50 us for one wave per token writing
+// the rows and the dots together; at 8192 tokens 411 us against 387 us for
+// that kernel, and the two launches above take 351 us.)
 constexpr int kBwdWaves = 8;
 constexpr int32_t kBwdWgMaxTokens = 2048;
 constexpr int kBwdThreads = kBwdWaves * kWave;
@@ -356,8 +335,7 @@ __global__ __launch_bounds__(kBwdThreads) void combine_backward_wg_kernel(
   const bool want_w = gw != nullptr;
   // per-lane rank tables (row_addr): the token's rows cost one round trip of
   // loads instead of a dependent chain, which matters at decode sizes; the
-  // one-wave kernel for large batches keeps the chain (the tables would cost
-  // it a wave per SIMD of occupancy and its long rows hide the chain)
+  // grad_w kernel for large batches keeps the chain (its long rows hide it)
   int32_t my_roff = 0;
   uint64_t my_g = 0, my_y = 0;
   if (lane < R) {
@@ -451,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(
     const int32_t *__restrict__ rank_offsets, int32_t *__restrict__ err, int64_t P, int32_t H,
     int32_t E, int32_t El, int64_t cap, RankCPtrs ry, uint16_t *__restrict__ out) {
   if (*err & kLayoutErrBits) return;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = wave_id(), lane = threadIdx.x % kWave;
   const int nch = H / 8;
   for (int64_t p = (int64_t)blockIdx.x * kRowWaves + wave; p < P;
        p += (int64_t)gridDim.x * kRowWaves) {
@@ -471,6 +449,12 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(
 // above, the chain form (see combine_chain_kernel).  About twice the waves
 // the GPU holds at once.
 constexpr int64_t kCombineTablesMaxUnits = 16384;
+// Large combines keep at most 12 workgroups per CU resident
+// (resident_cap_lds; their registers allow 20): at T=8192, H=7168, k=8
+// 179.9 against 181.6 us, with Zipf-skewed routing 172.0 against 176.7 us
+// (same process, interleaved; 16 per CU 179.8 and 174.7, 10 per CU 183.0
+// and 175.3).
+constexpr int kCombineWgPerCu = 12;
 
 hipError_t launch_combine(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
                           const RankCPtrs &ry, const float *w, const void *shared, void *out,
@@ -481,22 +465,23 @@ hipError_t launch_combine(const ep_config &c, const ep_layout_t &h, const int32_
   const int32_t El = c.num_experts / c.num_ranks;
   const uint16_t *sh = static_cast<const uint16_t *>(shared);
   uint16_t *o = static_cast<uint16_t *>(out);
+  const size_t lds = resident_cap_lds(units, kCombineWgPerCu);
   if (units <= kCombineTablesMaxUnits) {
     if (shared)
-      hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(kThreads), 0, s, topk_idx, h.slot_of,
-                         h.rank_offsets, h.error_flag, w, c.num_tokens, c.hidden, c.num_topk,
-                         c.num_experts, El, c.num_ranks, capacity_rows, ry, sh, o);
+      hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(kThreads), lds, s, topk_idx,
+                         h.slot_of, h.rank_offsets, h.error_flag, w, c.num_tokens, c.hidden,
+                         c.num_topk, c.num_experts, El, c.num_ranks, capacity_rows, ry, sh, o);
     else
-      hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(kThreads), 0, s, topk_idx,
+      hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(kThreads), lds, s, topk_idx,
                          h.slot_of, h.rank_offsets, h.error_flag, w, c.num_tokens, c.hidden,
                          c.num_topk, c.num_experts, El, c.num_ranks, capacity_rows, ry, nullptr, o);
   } else {
     if (shared)
-      hipLaunchKernelGGL(combine_chain_kernel<true>, dim3(grid), dim3(kThreads), 0, s, topk_idx,
+      hipLaunchKernelGGL(combine_chain_kernel<true>, dim3(grid), dim3(kThreads), lds, s, topk_idx,
                          h.slot_of, h.rank_offsets, h.error_flag, w, c.num_tokens, c.hidden,
                          c.num_topk, c.num_experts, El, capacity_rows, ry, sh, o);
     else
-      hipLaunchKernelGGL(combine_chain_kernel<false>, dim3(grid), dim3(kThreads), 0, s, topk_idx,
+      hipLaunchKernelGGL(combine_chain_kernel<false>, dim3(grid), dim3(kThreads), lds, s, topk_idx,
                          h.slot_of, h.rank_offsets, h.error_flag, w, c.num_tokens, c.hidden,
                          c.num_topk, c.num_experts, El, capacity_rows, ry, nullptr, o);
   }
@@ -516,12 +501,15 @@ hipError_t launch_combine_backward(const ep_config &c, const ep_layout_t &h,
                        c.num_topk, c.num_experts, c.num_experts / c.num_ranks, c.num_ranks,
                        capacity_rows, ry, rg, grad_w);
   } else {
-    const int grid = row_grid(c, c.num_tokens);
-    hipLaunchKernelGGL(combine_backward_wave_kernel, dim3(grid), dim3(kThreads), 0, s, topk_idx,
+    const hipError_t e =
+        launch_combine_backward_rows(c, h, topk_idx, grad_out, w, rg, capacity_rows, s);
+    if (e != hipSuccess || !grad_w) return e;
+    hipLaunchKernelGGL(combine_backward_dots_kernel, dim3(row_grid(c, c.num_tokens)),
+                       dim3(kThreads), 0, s, topk_idx,
                        h.slot_of, h.rank_offsets, h.error_flag,
-                       static_cast<const uint16_t *>(grad_out), w, c.num_tokens, c.hidden,
+                       static_cast<const uint16_t *>(grad_out), c.num_tokens, c.hidden,
                        c.num_topk, c.num_experts, c.num_experts / c.num_ranks, capacity_rows, ry,
-                       rg, grad_w);
+                       grad_w);
   }
   return hipGetLastError();
 }

@@ -14,6 +14,14 @@ namespace dev {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
+// This wave's index in its workgroup as a wave-uniform value.  threadIdx.x /
+// kWave is the same on every lane of a wave, but the compiler treats it as a
+// per-lane value, and so every work-unit index derived from it: 64-bit
+// divisions and loop control then run as vector instructions on every lane.
+__device__ inline int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+
 __device__ inline uint64_t readlane64(uint64_t v, int lane) {
   const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
   const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
@@ -180,6 +188,14 @@ __device__ inline uint32_t bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// 8 binary32 -> 8 bf16 (bf16_bits each), two per dword, channel order kept.
+__device__ inline u32x4 pack8(const float *acc) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = bf16_bits(acc[2 * i]) | (bf16_bits(acc[2 * i + 1]) << 16);
+  return o;
 }
 
 }  // namespace dev

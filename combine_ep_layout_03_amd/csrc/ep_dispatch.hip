@@ -46,31 +46,19 @@ constexpr int kThreads = kRowWaves * kWave;
 constexpr int kFp8SegBlocks = 8;  // 128-channel blocks per FP8 work unit (= 64 lanes x 16 ch)
 constexpr int kBf16SegChunks = 2 * kWave;  // 16-byte chunks per BF16 work unit (two per lane)
 
-// Large dispatches keep fewer of their waves resident: each workgroup
-// reserves LDS it never uses, so a CU holds at most 14 FP8 or 12 BF16
-// dispatch workgroups instead of the 32 its registers allow.  With every
-// wave's scattered row stores in flight at once the memory system queues
-// more than it can schedule well; fewer waves write faster.  Measured on
-// MI355X (same process, interleaved): FP8 at T=8192, H=7168, k=8 122.2 ->
-// 116.4 us (dispatch + combine 301.2 -> 296.1 us), Zipf-skewed routing
-// 116.9 -> 111.2 us, BF16 at the same shape 215.9 -> 204.3 us; 12 to 16
-// workgroups per CU all gain, 8 lose.  Below two rounds of the GPU's
-// resident waves a partly filled extra round can cost more than this gains
-// (FP8 at T=512: 9.7 us uncapped, 12.1 us at 12 per CU), so only launches of
-// at least kThrottleMinUnits units are capped.  (The SiLU re-quantization,
-// with more arithmetic per byte, is slower with fewer waves: 116 -> 124 us
-// at 16 per CU.)
-constexpr int64_t kThrottleMinUnits = 16384;
-constexpr int kLdsPerCu = 160 * 1024;  // gfx950
+// Large dispatches keep fewer of their waves resident (resident_cap_lds): a
+// CU holds at most 14 FP8 or 12 BF16 dispatch workgroups instead of the 32
+// their registers allow.  With every wave's scattered row stores in flight at
+// once the memory system queues more than it can schedule well; fewer waves
+// write faster.  Measured on MI355X (same process, interleaved): FP8 at
+// T=8192, H=7168, k=8 122.2 -> 116.4 us (dispatch + combine 301.2 -> 296.1
+// us), Zipf-skewed routing 116.9 -> 111.2 us, BF16 at the same shape 215.9 ->
+// 204.3 us; 12 to 16 workgroups per CU all gain, 8 lose.  Below two rounds of
+// the GPU's resident waves a partly filled extra round can cost more than
+// this gains (FP8 at T=512: 9.7 us uncapped, 12.1 us at 12 per CU), hence
+// kResidentCapMinUnits.  (The SiLU re-quantization, with more arithmetic per
+// byte, is slower with fewer waves: 116 -> 124 us at 16 per CU.)
 constexpr int kFp8WgPerCu = 14, kBf16WgPerCu = 12;
-
-// Dynamic LDS that lets a CU hold at most wg_per_cu of these workgroups
-// (rounded down to whole KiB, so an allocation granule of up to 1 KiB keeps
-// the count exact); 0 below kThrottleMinUnits.
-size_t throttle_lds(int64_t units, int wg_per_cu) {
-  if (units < kThrottleMinUnits) return 0;
-  return (size_t)(kLdsPerCu / wg_per_cu) / 1024 * 1024;
-}
 
 // The loads of a unit do not wait for one another: the error word (read once
 // per wave, checked before the first write), the per-lane rank tables, the
@@ -78,12 +66,18 @@ size_t throttle_lds(int64_t units, int wg_per_cu) {
 // together; the destination rows then come from row_addr's shuffles.  A row
 // outside the capacity (a stale handle) raises EP_DEVERR_ROW and the token is
 // skipped.
-__global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
-    const uint16_t *__restrict__ x, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ slot_of, const int32_t *__restrict__ rank_offsets,
-    int32_t *__restrict__ err, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El, int32_t R,
-    int64_t cap, RankPtrs rx) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+// The BF16 copies of a unit.  Scaled (combine's backward, whose gradient rows
+// are a dispatch of grad_out): copy j is bf16(RN32(w_j * x)), one binary32
+// multiply per element with w_j = w[t*k+j] (1 if w is NULL), loaded beside
+// the token's indices.
+template <bool Scaled>
+__device__ inline void bf16_rows(const uint16_t *__restrict__ x, const int32_t *__restrict__ idx,
+                                 const int32_t *__restrict__ slot_of,
+                                 const int32_t *__restrict__ rank_offsets,
+                                 int32_t *__restrict__ err, const float *__restrict__ w, int32_t T,
+                                 int32_t H, int32_t k, int32_t E, int32_t El, int32_t R,
+                                 int64_t cap, const RankPtrs &rx) {
+  const int wave = wave_id(), lane = threadIdx.x % kWave;
   const int nch = H / 8;  // 16-byte chunks per row
   const int nseg = (nch + kBf16SegChunks - 1) / kBf16SegChunks;
   const int64_t units = (int64_t)T * nseg;
@@ -98,9 +92,11 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     const int c1 = c0 + kWave;
     const bool ok0 = c0 < nch, ok1 = c1 < nch;
     int32_t e = -1, sl = 0;
+    float wj = 1.0f;
     if (lane < k) {
       e = idx[t * k + lane];
       sl = slot_of[t * k + lane];
+      if (Scaled && w) wj = w[t * k + lane];
     }
     int32_t my_roff = 0;
     uint64_t my_base = 0;
@@ -122,8 +118,22 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     if (__ballot(lane < k && dst == 0) != 0) return true;  // a bad row: write nothing for t
     for (int j = 0; j < k; ++j) {
       u32x4 *d = reinterpret_cast<u32x4 *>(readlane64(dst, j));
-      if (ok0) __builtin_nontemporal_store(v0, d + c0);
-      if (ok1) __builtin_nontemporal_store(v1, d + c1);
+      u32x4 o0 = v0, o1 = v1;
+      if (Scaled) {
+        const float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j));
+        float p0[8], p1[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p0[2 * i] = wv * __uint_as_float(v0[i] << 16);
+          p0[2 * i + 1] = wv * __uint_as_float(v0[i] & 0xFFFF0000u);
+          p1[2 * i] = wv * __uint_as_float(v1[i] << 16);
+          p1[2 * i + 1] = wv * __uint_as_float(v1[i] & 0xFFFF0000u);
+        }
+        o0 = pack8(p0);
+        o1 = pack8(p1);
+      }
+      if (ok0) __builtin_nontemporal_store(o0, d + c0);
+      if (ok1) __builtin_nontemporal_store(o1, d + c1);
     }
     return true;
   };
@@ -135,12 +145,29 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     unit(u, false);
 }
 
+__global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ slot_of, const int32_t *__restrict__ rank_offsets,
+    int32_t *__restrict__ err, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El, int32_t R,
+    int64_t cap, RankPtrs rx) {
+  bf16_rows<false>(x, idx, slot_of, rank_offsets, err, nullptr, T, H, k, E, El, R, cap, rx);
+}
+
+// Combine's backward: its gradient rows (ep_combine_backward).
+__global__ __launch_bounds__(kThreads) void combine_backward_rows_kernel(
+    const uint16_t *__restrict__ gout, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ slot_of, const int32_t *__restrict__ rank_offsets,
+    int32_t *__restrict__ err, const float *__restrict__ w, int32_t T, int32_t H, int32_t k,
+    int32_t E, int32_t El, int32_t R, int64_t cap, RankPtrs rg) {
+  bf16_rows<true>(gout, idx, slot_of, rank_offsets, err, w, T, H, k, E, El, R, cap, rg);
+}
+
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ slot_of, const int32_t *__restrict__ rank_offsets,
     int32_t *__restrict__ err, int32_t T, int32_t H, int32_t k, int32_t E, int32_t El, int32_t R,
     int64_t cap, RankPtrs rq, ScalePtrs rs) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = wave_id(), lane = threadIdx.x % kWave;
   const int nb = H / 128;  // 128-channel blocks per row
   const int nseg = (nb + kFp8SegBlocks - 1) / kFp8SegBlocks;
   const int64_t units = (int64_t)T * nseg;
@@ -202,6 +229,20 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
 
 }  // namespace
 
+hipError_t launch_combine_backward_rows(const ep_config &c, const ep_layout_t &h,
+                                        const int32_t *topk_idx, const void *grad_out,
+                                        const float *w, const RankPtrs &rg,
+                                        int64_t capacity_rows, hipStream_t s) {
+  const int64_t nseg = (c.hidden / 8 + kBf16SegChunks - 1) / kBf16SegChunks;
+  const int64_t units = (int64_t)c.num_tokens * nseg;
+  hipLaunchKernelGGL(combine_backward_rows_kernel, dim3(row_grid(c, units)), dim3(kThreads),
+                     resident_cap_lds(units, kBf16WgPerCu), s,
+                     static_cast<const uint16_t *>(grad_out), topk_idx, h.slot_of, h.rank_offsets,
+                     h.error_flag, w, c.num_tokens, c.hidden, c.num_topk, c.num_experts,
+                     c.num_experts / c.num_ranks, c.num_ranks, capacity_rows, rg);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
                            const void *x, const RankPtrs &rx, const ScalePtrs &rs,
                            int64_t capacity_rows, hipStream_t s) {
@@ -210,7 +251,7 @@ hipError_t launch_dispatch(const ep_config &c, const ep_layout_t &h, const int32
     const int64_t nseg = (c.hidden / 128 + kFp8SegBlocks - 1) / kFp8SegBlocks;
     const int64_t units = (int64_t)c.num_tokens * nseg;
     hipLaunchKernelGGL(dispatch_fp8_kernel, dim3(row_grid(c, units)), dim3(kThreads),
-                       throttle_lds(units, kFp8WgPerCu), s,
+                       resident_cap_lds(units, kFp8WgPerCu), s,
                        static_cast<const uint16_t *>(x), topk_idx, h.slot_of, h.rank_offsets,
                        h.error_flag, c.num_tokens, c.hidden, c.num_topk, c.num_experts, El,
                        c.num_ranks, capacity_rows, rx, rs);
@@ -218,7 +259,7 @@ hipError_t launch_dispatch(const ep_config &c, const ep_layout_t &h, const int32
     const int64_t nseg = (c.hidden / 8 + kBf16SegChunks - 1) / kBf16SegChunks;
     const int64_t units = (int64_t)c.num_tokens * nseg;
     hipLaunchKernelGGL(dispatch_bf16_kernel, dim3(row_grid(c, units)), dim3(kThreads),
-                       throttle_lds(units, kBf16WgPerCu), s,
+                       resident_cap_lds(units, kBf16WgPerCu), s,
                        static_cast<const uint16_t *>(x), topk_idx, h.slot_of, h.rank_offsets,
                        h.error_flag, c.num_tokens, c.hidden, c.num_topk, c.num_experts, El,
                        c.num_ranks, capacity_rows, rx);

@@ -83,6 +83,14 @@ hipError_t launch_dispatch(const ep_config &c, const ep_layout_t &h, const int32
                            const void *x, const RankPtrs &rx, const ScalePtrs &rs,
                            int64_t capacity_rows, hipStream_t s);
 
+// The gradient rows of combine's backward, bf16(RN32(w[p] * grad_out[t])) into
+// each pair's row (w NULL: weights 1): the BF16 dispatch with one multiply
+// per copy (ep_dispatch.hip).
+hipError_t launch_combine_backward_rows(const ep_config &c, const ep_layout_t &h,
+                                        const int32_t *topk_idx, const void *grad_out,
+                                        const float *w, const RankPtrs &rg,
+                                        int64_t capacity_rows, hipStream_t s);
+
 hipError_t launch_combine(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
                           const RankCPtrs &ry, const float *w, const void *shared, void *out,
                           int64_t capacity_rows, hipStream_t s);
@@ -115,6 +123,21 @@ hipError_t launch_route_layout(const ep_config &c, const ep_router_t &rt, const 
 
 hipError_t launch_unpermute(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
                             const RankCPtrs &ry, void *out, int64_t capacity_rows, hipStream_t s);
+
+// Resident-workgroup cap of the large streaming launches (dispatch, combine,
+// the backward's gradient rows): dynamic LDS that the kernel never touches,
+// sized so a CU holds at most wg_per_cu of these single-wave workgroups
+// (gfx950: 160 KiB of LDS per CU; rounded down to whole KiB, so an allocation
+// granule of up to 1 KiB keeps the count exact).  Launches of fewer than
+// kResidentCapMinUnits work units (about two rounds of the waves the GPU
+// holds) are not capped: there a partly filled extra round can cost more
+// than the cap gains.  Only timing depends on it.
+constexpr int64_t kResidentCapMinUnits = 16384;
+constexpr int kLdsPerCu = 160 * 1024;
+inline size_t resident_cap_lds(int64_t units, int wg_per_cu) {
+  if (units < kResidentCapMinUnits) return 0;
+  return (size_t)(kLdsPerCu / wg_per_cu) / 1024 * 1024;
+}
 
 // Grid size of the per-row kernels: num_workgroups, else one single-wave
 // workgroup per work unit (the kernels grid-stride over the rest, if any).

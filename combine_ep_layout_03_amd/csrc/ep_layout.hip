@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(const int32_t *_
                                                                  int32_t *__restrict__ hist,
                                                                  int32_t *__restrict__ err) {
   extern __shared__ int32_t lds[];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = dev::wave_id(), lane = threadIdx.x % kWave;
   if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
   const int E1 = E + 1;
   int32_t *h = lds + wave * E1;

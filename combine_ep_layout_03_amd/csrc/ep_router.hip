@@ -360,7 +360,7 @@ __global__ __launch_bounds__(COUNT ? kWave * kRouteCountWaves : kWave) void rout
     for (int e = threadIdx.x; e <= E; e += kWave * kRouteCountWaves) cnt[e] = 0;
     __syncthreads();
     const int64_t c0 = (int64_t)blockIdx.x * tpc;
-    tb0 = c0 + (int64_t)(threadIdx.x / kWave) * kRowTokens;
+    tb0 = c0 + (int64_t)wave_id() * kRowTokens;
     tend = (c0 + tpc < T) ? c0 + tpc : T;
     tstep = kRouteCountStep;
   }
