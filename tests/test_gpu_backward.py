@@ -133,6 +133,45 @@ def test_combine_backward_grid_size_invariance():
         assert np.array_equal(gwn.view(np.uint32), outs[0][1].view(np.uint32))
 
 
+@pytest.mark.parametrize("nwg", [0, 7, 300])
+def test_combine_backward_two_launch_form(nwg):
+    """T >= 2048 takes two launches (the gradient rows as a weighted BF16
+    dispatch, then grad_w alone).  k = 12 > 8 runs the grad_w kernel's second
+    block of pairs, H = 1544 (193 chunks) leaves the last 128-chunk unit
+    ragged, and the results are bit-identical for any grid size."""
+    from test_gpu_parity import custom
+    T, H, k, E, R = 2100, 1544, 12, 24, 4
+    rng = np.random.default_rng(21)
+    w = custom("bw2", T, H, k, E, R, False, rng.integers(0, E, (T, k)), seed=21)
+    run = GpuRun(w, num_workgroups=nwg).layout()
+    L = oracle.layout(w.topk_idx, w.E, w.R)
+    y = make_expert_rows(w.P, w.H)
+    ys = [y[L.rank_offsets[r]:L.rank_offsets[r + 1]] for r in range(w.R)]
+    say(f"combine_backward two launches T={T} H={H} k={k} num_workgroups={nwg}")
+    check_backward(w, run, L, ys)
+    check_backward(w, run, L, ys, weights=False, with_w=False)
+
+
+def test_combine_backward_two_launch_form_after_a_bad_index():
+    """An index outside [0,E) stops both launches of the large-batch backward:
+    no gradient row and no grad_w is written."""
+    from test_gpu_parity import custom
+    T, H, k, E, R = 2048, 256, 4, 16, 4
+    idx = np.random.default_rng(4).integers(0, E, (T, k))
+    idx[1500, 2] = -3
+    w = custom("bad2", T, H, k, E, R, False, idx)
+    run = GpuRun(w).layout()
+    assert int(run.handle_np()["error_flag"][0]) & ep.EP_DEVERR_INDEX
+    say("combine_backward two launches after a bad index")
+    ones = lambda *shape: to_dev(bf16_from_f32(np.ones(shape, np.float32)))
+    ys = [ones(run.cap, H) for _ in range(R)]
+    grows = [torch.full((run.cap, H), 0x5A5A, dtype=torch.int16, device="cuda") for _ in range(R)]
+    gw = torch.full((T, k), 7.0, dtype=torch.float32, device="cuda")
+    ep.ep_combine_backward(run.cfg, run.h, run.idx, ones(T, H), run.wts, ys, grows, gw, run.cap)
+    torch.cuda.synchronize()
+    assert all(torch.all(g == 0x5A5A) for g in grows) and torch.all(gw == 7.0)
+
+
 def test_dispatch_backward_is_unit_weight_combine():
     """The backward of dispatch: sum each token's k gradient rows (ep_combine
     with unit weights) equals the oracle's unit-weight combine."""

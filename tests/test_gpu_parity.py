@@ -165,9 +165,10 @@ def test_stale_handle_rows_are_rejected_on_device():
     assert all(np.all(a.view(np.uint8) == POISON) for a in xs)
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("nwg", [0, 1, 3])
-def test_partly_stale_handle_skips_only_the_bad_tokens(fp8, nwg):
+@pytest.mark.parametrize("fp8,nwg,T", [(False, 0, 64), (False, 1, 64), (False, 3, 64),
+                                        (True, 0, 64), (True, 1, 64), (True, 3, 64),
+                                        (False, 0, 2048), (True, 3, 2048)])
+def test_partly_stale_handle_skips_only_the_bad_tokens(fp8, nwg, T):
     """A handle laid out with every pair on expert 0 (rank 0), then used with
     indices that move the second half of the tokens to rank R-1: their rows
     fall outside rank R-1's range and are skipped with EP_DEVERR_ROW, while
@@ -175,9 +176,10 @@ def test_partly_stale_handle_skips_only_the_bad_tokens(fp8, nwg):
     under the original routing.  Only the layout's error bits stop a call, so
     the row error one wave raises changes nothing another wave writes, nor
     (num_workgroups 1 or 3: each wave takes many units in turn) what the same
-    wave writes later, nor what a later call writes."""
-    T, H, k, E, R = 64, 256, 2, 8, 4
-    say(f"partly stale handle fp8={fp8} num_workgroups={nwg}")
+    wave writes later, nor what a later call writes.  T = 2048 takes the
+    combine backward's two-launch form (gradient rows, then grad_w)."""
+    H, k, E, R = 256, 2, 8, 4
+    say(f"partly stale handle fp8={fp8} num_workgroups={nwg} T={T}")
     w = custom("stale_half", T, H, k, E, R, fp8, np.zeros((T, k)))
     run = GpuRun(w, num_workgroups=nwg).layout()
     L = check_layout(w, run)
@@ -213,8 +215,8 @@ def test_partly_stale_handle_skips_only_the_bad_tokens(fp8, nwg):
     u = u16(run.unpermute())
     assert np.array_equal(u[:n], oracle.unpermute(ys, w.topk_idx, L)[:n])
     assert np.all(u[n:].view(np.uint8) == POISON)
-    # combine backward (one-wave or workgroup kernel by T): the good tokens'
-    # gradient rows and weight gradients, nothing for the others
+    # combine backward (two launches or one workgroup kernel by T): the good
+    # tokens' gradient rows and weight gradients, nothing for the others
     rng = np.random.default_rng(3)
     g = bf16_from_f32(rng.standard_normal((T, H), dtype=np.float32))
     grows = [torch.full((run.cap, H), -21846, dtype=torch.int16, device="cuda") for _ in range(R)]
