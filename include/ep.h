@@ -67,6 +67,13 @@
  *     EP_DEVERR_ROW set, and every other token is written, so what a call
  *     writes does not depend on the order its waves run in.
  *   - Output bytes do not depend on ep_config.num_workgroups.
+ *   - Resources: the row kernels run single-wave workgroups.  Dispatch,
+ *     combine and the large-batch combine backward launches of 16384 work
+ *     units or more (a unit is one token's 1024-channel segment) reserve 11
+ *     to 13 KiB of LDS per workgroup that the kernels never touch, which caps
+ *     how many of their workgroups a CU holds (fewer waves in flight move
+ *     their scattered rows faster); kernels running beside them on the same
+ *     CUs see that LDS as taken.
  *
  * Data types: routing indices int32 [T,k] row-major; weights fp32 [T,k];
  * activations bf16 as 16-bit patterns; FP8 is OCP E4M3 ("fn", max 448) one
