@@ -383,6 +383,29 @@ def test_combine_small_ragged(T, H, k, E, R):
     assert check_combine(w, run, L, ys) == 0
 
 
+@pytest.mark.parametrize("T,fp8", [(2400, False), (2340, True), (2341, True)])
+def test_launches_with_the_resident_workgroup_cap(T, fp8):
+    """Launches of at least 16384 work units (a unit is one token's 1024
+    channels) reserve unused LDS to cap resident workgroups; the bytes must
+    not change.  H = 7168 gives 7 units per token: T = 2400 caps the BF16
+    dispatch, the chain-form combine and the backward's gradient rows;
+    T = 2340 (16380 units) and 2341 (16387) sit either side of the threshold
+    for the FP8 dispatch and the combine."""
+    from test_gpu_backward import check_backward
+    H, k, E, R = 7168, 4, 32, 4
+    rng = np.random.default_rng(T)
+    w = custom("cap", T, H, k, E, R, fp8, rng.integers(0, E, (T, k)), seed=T)
+    say(f"resident-cap launches T={T} fp8={fp8} units={T * 7}")
+    run = GpuRun(w).layout().dispatch()
+    L = check_layout(w, run)
+    check_dispatch(w, run, L)
+    ys = expert_rows_for(w, L)
+    run.put_expert_rows(ys).combine()
+    assert check_combine(w, run, L, ys) == 0
+    if not fp8:
+        check_backward(w, run, L, ys)
+
+
 # ------------------------------------------------- determinism, reuse, graphs
 @pytest.mark.parametrize("name", ["ds16b", "decode"])
 def test_outputs_do_not_depend_on_num_workgroups(name):
