@@ -24,6 +24,9 @@
 //         correctly rounded binary32 a/448 and every code is E4M3 of the
 //         correctly rounded binary32 quotient x/s; the lane that holds a
 //         block's first channels writes its scale into each copy.
+// The gradient rows of combine's backward are the BF16 form with one multiply
+// per copy (combine_backward_rows_kernel): the backward of combine is a
+// dispatch of grad_out.
 // (Measured on MI355X at T=8192, H=7168, k=8: one-wave units beat one wave per
 // token, four-wave workgroups, token-per-workgroup with LDS-staged scales,
 // copy-per-wave splits and plain stores; the scattered row stores, not the
@@ -66,6 +69,7 @@ constexpr int kFp8WgPerCu = 14, kBf16WgPerCu = 12;
 // together; the destination rows then come from row_addr's shuffles.  A row
 // outside the capacity (a stale handle) raises EP_DEVERR_ROW and the token is
 // skipped.
+//
 // The BF16 copies of a unit.  Scaled (combine's backward, whose gradient rows
 // are a dispatch of grad_out): copy j is bf16(RN32(w_j * x)), one binary32
 // multiply per element with w_j = w[t*k+j] (1 if w is NULL), loaded beside
