@@ -450,10 +450,11 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(
 // the GPU holds at once.
 constexpr int64_t kCombineTablesMaxUnits = 16384;
 // Large combines keep at most 12 workgroups per CU resident
-// (resident_cap_lds; their registers allow 20): at T=8192, H=7168, k=8
-// 179.9 against 181.6 us, with Zipf-skewed routing 172.0 against 176.7 us
-// (same process, interleaved; 16 per CU 179.8 and 174.7, 10 per CU 183.0
-// and 175.3).
+// (resident_cap_lds; the plain combine's registers allow 20, the
+// shared-expert form's 16): at T=8192, H=7168, k=8 179.9 against 181.6 us,
+// with Zipf-skewed routing 172.0 against 176.7 us (same process,
+// interleaved; 16 per CU 179.8 and 174.7, 10 per CU 183.0 and 175.3); the
+// shared-expert form took 196-197 us with and without the cap.
 constexpr int kCombineWgPerCu = 12;
 
 hipError_t launch_combine(const ep_config &c, const ep_layout_t &h, const int32_t *topk_idx,
