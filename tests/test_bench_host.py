@@ -74,3 +74,43 @@ def test_a_failing_secondary_figure_does_not_cost_the_line(capsys):
     got = bench.guarded("configs.tiny", boom)
     assert set(got) == {"error"} and "no such kernel" in got["error"]
     assert "configs.tiny failed" in capsys.readouterr().err
+
+
+def test_kernel_keys_name_every_kernel():
+    """The profile summaries find kernels by the KERNEL_KEYS patterns, applied
+    to the names the kernel trace prints (namespace::name<template args>(...)).
+    Every __global__ kernel of the HIP sources but the debug un-permute must
+    match one pattern, in each template form it is launched with, so a
+    renamed or new kernel cannot drop out of profiles/ unnoticed; and every
+    pattern must match some kernel."""
+    import glob
+    import re
+    csrc = os.path.join(ROOT, "combine_ep_layout_03_amd", "csrc")
+    src = "".join(open(f).read() for f in sorted(glob.glob(os.path.join(csrc, "*.hip"))))
+    kernels = {}
+    decl = r"(template\s*<([^>]*)>\s*)?__global__\s+__launch_bounds__\([^)]*\)\s+void\s+(\w+)\s*\("
+    for m in re.finditer(decl, src):
+        params = m.group(2)
+        if params is None:
+            forms = [""]
+        else:
+            # one instance per template form the launchers use
+            n = params.count(",") + 1
+            if n == 1 and "bool" in params:
+                forms = ["<true>", "<false>"]
+            elif n == 1:
+                forms = ["<4>", "<16>"]
+            else:
+                forms = ["<16, true>", "<16, false>"]
+        kernels[m.group(3)] = forms
+    assert len(kernels) >= 15, sorted(kernels)
+    keys = list(bench.KERNEL_KEYS.values())
+    for name, forms in kernels.items():
+        if name == "unpermute_kernel":
+            continue
+        for f in forms:
+            printed = f"ep::(anonymous namespace)::{name}{f}(int const*, int)"
+            assert any(re.search(k, printed) for k in keys), printed
+    for k in keys:
+        assert any(re.search(k, f"ep::(anonymous namespace)::{n}{f}(int const*)")
+                   for n, forms in kernels.items() for f in forms), k
